@@ -1,0 +1,95 @@
+"""Seeded synthetic inputs shared by the oracle side and the GPU side.
+
+This module holds no attention arithmetic: it only names the workloads and
+draws their fp16 tensors, so that the HIP path and the oracle are fed the very
+same bits. Nothing here imports either of them.
+
+Recipe (one generator per tensor):
+    numpy.random.Generator(PCG64(seed)).standard_normal(shape, float64) * sigma
+    -> .astype(float16) (round to nearest even)
+with seed = 1000*config + {0: Q, 1: K, 2: V}. Causal and non-causal runs of a
+config share the same tensors.
+
+The workloads are the shapes the FlashAttention-2 teaching page measures
+(fp16 Q, K, V in [B,H,N,D], head dim 64, scale 1/8, iid inputs, plus a
+"concentrated softmax" input made by enlarging Q and K) widened to the sizes
+below; there is no public dataset behind them.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+
+@dataclass(frozen=True)
+class Workload:
+    cid: int            # workload number, 1..5
+    name: str
+    B: int
+    H: int
+    S: int
+    D: int
+    causal_modes: tuple  # which of (False, True) the workload is run in
+    sigma_qk: float      # standard deviation of Q and K entries
+    sigma_v: float       # standard deviation of V entries
+
+    @property
+    def scale(self) -> float:
+        """The softmax scale as the float32 value the kernel receives."""
+        return float(np.float32(1.0 / np.sqrt(float(self.D))))
+
+    @property
+    def shape(self):
+        return (self.B, self.H, self.S, self.D)
+
+    def flops(self, causal: bool) -> float:
+        """Attention FLOP count 4*B*H*S^2*D, halved when causal."""
+        f = 4.0 * self.B * self.H * self.S * self.S * self.D
+        return f / 2 if causal else f
+
+
+WORKLOADS = {
+    1: Workload(1, "tiny B1 H1 S128 D64", 1, 1, 128, 64, (False, True), 1.0, 1.0),
+    2: Workload(2, "B4 H8 S4096 D64", 4, 8, 4096, 64, (False, True), 1.0, 1.0),
+    3: Workload(3, "B2 H16 S8192 D128", 2, 16, 8192, 128, (True,), 1.0, 1.0),
+    4: Workload(4, "B16 H12 S1000 D64 concentrated", 16, 12, 1000, 64, (False, True), 3.0, 1.0),
+    5: Workload(5, "long B1 H32 S16384 D64", 1, 32, 16384, 64, (True,), 1.0, 1.0),
+}
+
+
+def normal_f16(seed: int, shape, sigma: float = 1.0) -> np.ndarray:
+    """iid N(0, sigma^2) values rounded to fp16."""
+    g = np.random.Generator(np.random.PCG64(seed))
+    return (g.standard_normal(shape, dtype=np.float64) * sigma).astype(np.float16)
+
+
+def make_inputs(cid: int):
+    """(q, k, v) fp16 arrays of shape [B,H,S,D] for workload ``cid``."""
+    w = WORKLOADS[cid]
+    q = normal_f16(1000 * cid + 0, w.shape, w.sigma_qk)
+    k = normal_f16(1000 * cid + 1, w.shape, w.sigma_qk)
+    v = normal_f16(1000 * cid + 2, w.shape, w.sigma_v)
+    return q, k, v
+
+
+def make_random(seed: int, B: int, H: int, S: int, D: int, sigma_qk: float = 1.0,
+                sigma_v: float = 1.0):
+    """(q, k, v) for an arbitrary shape, seeds seed+0/1/2."""
+    shape = (B, H, S, D)
+    return (normal_f16(seed, shape, sigma_qk), normal_f16(seed + 1, shape, sigma_qk),
+            normal_f16(seed + 2, shape, sigma_v))
+
+
+def sample_rows(cid: int, n: int, seed: int = 7) -> np.ndarray:
+    """Flat row indices (b*H+h)*S+i for sampled checks: the first and last row
+    of every head's first and last query block plus ``n`` uniform picks."""
+    w = WORKLOADS[cid]
+    g = np.random.Generator(np.random.PCG64(seed + 31 * cid))
+    heads = w.B * w.H
+    fixed = []
+    for hd in (0, heads - 1):
+        for i in (0, 1, w.S - 2, w.S - 1):
+            fixed.append(hd * w.S + i)
+    picks = g.integers(0, heads * w.S, size=n)
+    return np.unique(np.concatenate([np.array(fixed, dtype=np.int64), picks.astype(np.int64)]))
