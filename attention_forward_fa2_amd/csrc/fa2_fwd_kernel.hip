@@ -40,6 +40,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "fa2_internal.h"
 
 namespace fa2 {
@@ -47,6 +49,7 @@ namespace {
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+typedef _Float16 half2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
@@ -57,6 +60,9 @@ constexpr double kLog2e = 1.44269504088896340736;
 // Finite start value of the running max: exp2((m0 - m) * c) is exactly 0 for any
 // real score m, and a row whose keys were all masked so far keeps alpha = 1, p = 0.
 constexpr float kMaxInit = -1.0e30f;
+// A lane's partial row sum of fp16 probabilities below this bound means none of
+// them overflowed fp16 (largest finite 65504).
+constexpr float kSpeculateLimit = 32768.0f;
 
 template <int D_, int QB_, int NW_, int BN_>
 struct Shape {
@@ -75,6 +81,8 @@ struct Shape {
     static constexpr int TILE = BN * D;       // halves per K or V tile
     static constexpr int LOADS = TILE / 8 / 64 / NW;  // 16-byte loads per lane per tensor per tile
     static constexpr int LDS_BYTES = 2 /*stages*/ * 2 /*K,V*/ * TILE * 2;
+    // Occupancy the register allocation targets (waves per SIMD).
+    static constexpr int WAVES_PER_SIMD = (D == 64 && QB <= 2) ? 4 : (QB <= 2 ? 2 : 1);
     static_assert(BN % 32 == 0 && D % 32 == 0, "tile shape");
     static_assert((TILE / 8) % (64 * NW) == 0, "loads must divide evenly among lanes");
 };
@@ -112,6 +120,41 @@ __device__ __forceinline__ float sum_xor32(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Direct-to-LDS 16-byte loads. Lane i's 16 bytes land at LDS byte address
+// lds_base + 16*i (lds_base must be wave-uniform). Written as inline asm so the
+// compiler does not track them: its own tracking of these loads would make every
+// later LDS read of the other ring stage wait for them, which removes the
+// overlap of the next tile's load with this tile's math. The kernel waits for
+// them itself (vmcnt(0)) before the barrier that publishes a stage. M0 carries
+// the LDS base; nothing else in this kernel uses M0.
+//   dma_16B_s: address = 64-bit wave-uniform base (SGPRs) + 32-bit lane offset.
+//   dma_16B_v: full 64-bit per-lane address.
+__device__ __forceinline__ void dma_16B_s(const void* sbase, uint32_t voff, uint32_t lds_base) {
+    asm volatile(
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %0, %1"
+        :
+        : "v"(voff), "s"(sbase), "s"(lds_base)
+        : "memory");
+}
+__device__ __forceinline__ void dma_16B_v(const void* src, uint32_t lds_base) {
+    asm volatile(
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %0, off"
+        :
+        : "v"(src), "s"(lds_base)
+        : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(lds_void*)p;
+}
+
+template <int V>
+using Int = std::integral_constant<int, V>;
+
 struct KernelArgs {
     const _Float16* q;
     const _Float16* k;
@@ -125,15 +168,22 @@ struct KernelArgs {
     float c;       // scale * log2(e)
 };
 
+// Raise the wave priority around the MFMA blocks so the arbiter keeps the matrix
+// unit fed from whichever wave has MFMAs ready (a scheduling hint only).
+#ifndef FA2_SETPRIO
+#define FA2_SETPRIO 1
+#endif
+
 template <class SH, bool CAUSAL>
-__global__ __launch_bounds__(SH::THREADS) void fa2_fwd_kernel(KernelArgs a) {
+__global__ __launch_bounds__(SH::THREADS) __attribute__((amdgpu_waves_per_eu(SH::WAVES_PER_SIMD)))
+void fa2_fwd_kernel(KernelArgs a) {
     constexpr int D = SH::D, QB = SH::QB, NW = SH::NW, BN = SH::BN, QW = SH::QW, BM = SH::BM;
     constexpr int NKB = SH::NKB, NKC = SH::NKC, DK = SH::DK, DB = SH::DB, CPR = SH::CPR;
-    constexpr int TILE = SH::TILE;
+    constexpr int TILE = SH::TILE, LOADS = SH::LOADS;
 
+    // LDS ring: [stage][K | V][TILE] halves.
     extern __shared__ __attribute__((aligned(16))) _Float16 smem[];
-    // [stage][K | V][TILE]
-    _Float16* const lds = smem;
+    const uint32_t lds_base = __builtin_amdgcn_readfirstlane(lds_addr(smem));
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -163,6 +213,52 @@ __global__ __launch_bounds__(SH::THREADS) void fa2_fwd_kernel(KernelArgs a) {
     const int q0 = qt * BM;
     const int qw0 = q0 + wave * QW;
 
+    int n_tiles = (S + BN - 1) / BN;
+    if (CAUSAL) n_tiles = min(n_tiles, (min(q0 + BM, S) - 1) / BN + 1);
+
+    // Per-lane source offsets (bytes, within a tile) of this lane's direct-to-LDS
+    // loads: load i fills LDS chunk c = (i*NW + wave)*64 + lane, i.e. tile row
+    // r = c / CPR and physical chunk pc = c % CPR, from the logical chunk
+    // pc ^ swz(r) of key row k0 + r. Loop-invariant; the tile base is scalar.
+    uint32_t offK[LOADS], offV[LOADS];
+    int rowL[LOADS];
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+        const int c = (i * NW + wave) * 64 + lane;
+        const int r = c / CPR, pc = c % CPR;
+        rowL[i] = r;
+        offK[i] = 2u * (r * D + 8 * (pc ^ swz_k<D>(r)));
+        offV[i] = 2u * (r * D + 8 * (pc ^ swz_v<D>(r)));
+    }
+
+    // Issue the direct-to-LDS loads of K/V tile t into ring stage ST. Rows past
+    // the end of the sequence (only in the last tile) are clamped to row S-1;
+    // their scores are masked to -inf before use.
+    auto issue_tile = [&](int t, auto st_c) {
+        constexpr int ST = decltype(st_c)::value;
+        const int k0 = t * BN;
+        if (k0 + BN <= S) {
+            const _Float16* kt = Kh + (long long)k0 * D;
+            const _Float16* vt = Vh + (long long)k0 * D;
+#pragma unroll
+            for (int i = 0; i < LOADS; ++i) {
+                const uint32_t dst = lds_base + 2u * (i * NW + wave) * 512;
+                dma_16B_s(kt, offK[i], dst + 2u * (ST * 2 + 0) * TILE);
+                dma_16B_s(vt, offV[i], dst + 2u * (ST * 2 + 1) * TILE);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < LOADS; ++i) {
+                const uint32_t dst = lds_base + 2u * (i * NW + wave) * 512;
+                const long long shift = (long long)(min(k0 + rowL[i], S - 1) - rowL[i]) * D;
+                dma_16B_v((const char*)(Kh + shift) + offK[i], dst + 2u * (ST * 2 + 0) * TILE);
+                dma_16B_v((const char*)(Vh + shift) + offV[i], dst + 2u * (ST * 2 + 1) * TILE);
+            }
+        }
+    };
+
+    issue_tile(0, Int<0>{});
+
     // Q^T as the B operand of the score MFMA, kept in registers for the whole scan.
     // Rows past the end are clamped (their results are never stored).
     half8 qreg[QB][DK];
@@ -173,6 +269,11 @@ __global__ __launch_bounds__(SH::THREADS) void fa2_fwd_kernel(KernelArgs a) {
         for (int kk = 0; kk < DK; ++kk)
             qreg[qb][kk] = *reinterpret_cast<const half8*>(Qh + (long long)row * D + 32 * kk + 8 * g);
     }
+    // Wait for Q here with the compiler-visible s_waitcnt (vmcnt(0), expcnt and
+    // lgkmcnt unconstrained): otherwise the compiler's wait for Q sits at its
+    // first use inside the loop and, since vmcnt also counts the K/V loads of the
+    // next tile, would stall on them every iteration.
+    __builtin_amdgcn_s_waitcnt(0x0F70);
 
     f32x4 oacc[DB][QB];
 #pragma unroll
@@ -185,46 +286,42 @@ __global__ __launch_bounds__(SH::THREADS) void fa2_fwd_kernel(KernelArgs a) {
         m_run[qb] = kMaxInit;
         l_run[qb] = 0.f;
     }
+    const half2 kOnes2 = half2{(_Float16)1.0f, (_Float16)1.0f};
 
-    int n_tiles = (S + BN - 1) / BN;
-    if (CAUSAL) n_tiles = min(n_tiles, (min(q0 + BM, S) - 1) / BN + 1);
-
-    // Issue the direct-to-LDS loads of K/V tile t into ring stage st. Lane `lane`
-    // of load instruction `inst` fills LDS chunk inst*64+lane, i.e. row r and
-    // physical chunk pc; it fetches the logical chunk pc ^ swz(r) of key row
-    // k0 + r (clamped to S-1: such rows are masked to -inf before use).
-    auto issue_tile = [&](int t, int st) {
-        const int k0 = t * BN;
-        _Float16* const ldsK = lds + (st * 2 + 0) * TILE;
-        _Float16* const ldsV = lds + (st * 2 + 1) * TILE;
+    // LDS read offsets (bytes) that do not depend on the tile: the K swizzle of
+    // rows 16*kb + l16 depends on l16 only, the V swizzle of rows
+    // 32*kc + 4g + l16/4 (+16) on g and l16 only.
+    uint32_t rdK[DK];
 #pragma unroll
-        for (int i = 0; i < SH::LOADS; ++i) {
-            const int inst = i * NW + wave;
-            const int c = inst * 64 + lane;
-            const int r = c / CPR, pc = c % CPR;
-            const long long grow = min(k0 + r, S - 1);
-            const _Float16* srcK = Kh + grow * D + 8 * (pc ^ swz_k<D>(r));
-            const _Float16* srcV = Vh + grow * D + 8 * (pc ^ swz_v<D>(r));
-            __builtin_amdgcn_global_load_lds(srcK, (lds_void*)(ldsK + inst * 512), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds(srcV, (lds_void*)(ldsV + inst * 512), 16, 0, 0);
+    for (int kk = 0; kk < DK; ++kk) rdK[kk] = 2u * (l16 * D + 8 * ((4 * kk + g) ^ swz_k<D>(l16)));
+    uint32_t rdV[DB];
+    {
+        const int r0 = 4 * g + (l16 >> 2);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+            const int lc = 2 * db + ((l16 & 3) >> 1);
+            rdV[db] = 2u * (r0 * D + 8 * (lc ^ swz_v<D>(r0)) + 4 * (l16 & 1));
         }
-    };
+    }
 
-    issue_tile(0, 0);
-    for (int t = 0; t < n_tiles; ++t) {
-        const int st = t & 1;
-        // Tile t is resident for every wave, and every wave has finished reading
-        // stage st^1 (tile t-1), which the next loads overwrite.
+    // One step of the scan over key tile t held in ring stage ST.
+    auto tile_step = [&](int t, auto st_c) {
+        constexpr int ST = decltype(st_c)::value;
+        // Tile t is resident for every wave (each waits for its own loads, then
+        // the barrier), and every wave has finished reading the other stage
+        // (tile t-1), which the next loads overwrite.
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
-        if (t + 1 < n_tiles) issue_tile(t + 1, st ^ 1);
+        if (t + 1 < n_tiles) issue_tile(t + 1, Int<1 - ST>{});
 
         const int k0 = t * BN;
-        if (CAUSAL && k0 > qw0 + QW - 1) continue;  // tile lies above this wave's diagonal
+        if (CAUSAL && k0 > qw0 + QW - 1) return;  // tile lies above this wave's diagonal
 
-        const _Float16* const ldsK = lds + (st * 2 + 0) * TILE;
-        const _Float16* const ldsV = lds + (st * 2 + 1) * TILE;
+        const char* const ldsK = reinterpret_cast<const char*>(smem) + 2 * (ST * 2 + 0) * TILE;
+        const char* const ldsV = reinterpret_cast<const char*>(smem) + 2 * (ST * 2 + 1) * TILE;
 
         // ---- S^T = K Q^T on MFMA ----
+        if (FA2_SETPRIO) __builtin_amdgcn_s_setprio(1);
         f32x4 sacc[QB][NKB];
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
@@ -232,16 +329,15 @@ __global__ __launch_bounds__(SH::THREADS) void fa2_fwd_kernel(KernelArgs a) {
             for (int kb = 0; kb < NKB; ++kb) sacc[qb][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
-            const int r = 16 * kb + l16;
 #pragma unroll
             for (int kk = 0; kk < DK; ++kk) {
-                const int lc = 4 * kk + g;
-                const half8 ka = *reinterpret_cast<const half8*>(ldsK + r * D + 8 * (lc ^ swz_k<D>(r)));
+                const half8 ka = *reinterpret_cast<const half8*>(ldsK + rdK[kk] + kb * 16 * D * 2);
 #pragma unroll
                 for (int qb = 0; qb < QB; ++qb)
                     sacc[qb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qreg[qb][kk], sacc[qb][kb], 0, 0, 0);
             }
         }
+        if (FA2_SETPRIO) __builtin_amdgcn_s_setprio(0);
 
         // ---- masks: keys past the end, and keys after the query when causal ----
         const bool need_mask = (k0 + BN > S) || (CAUSAL && k0 + BN - 1 > qw0);
@@ -260,56 +356,88 @@ __global__ __launch_bounds__(SH::THREADS) void fa2_fwd_kernel(KernelArgs a) {
         }
 
         // ---- online softmax update ----
+        // Probabilities are taken against the running reference m_run:
+        // p = 2^(s*c - m_run*c). l and o always use the same reference per row,
+        // so O = o/l and LSE = scale*m_run + ln l hold for any reference; the
+        // reference only has to keep every p representable in fp16. The
+        // common path therefore skips the tile max: it exponentiates against
+        // the current reference and accepts the tile if every lane's partial
+        // row sum of the fp16 p stays below 2^15 (so no p overflowed). The
+        // first tile, or a tile that fails the check, takes the row max of the
+        // tile (combined over the 4 lanes of a query), moves the reference to
+        // max(m_run, tile max), rescales o and l by alpha = 2^((m_old - m_new)*c)
+        // and exponentiates again: the update of the online softmax.
         half8 pb[QB][NKC];
+        float rs[QB];
+        auto exponentiate = [&]() {
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-            float mx = sacc[qb][0][0];
+            for (int qb = 0; qb < QB; ++qb) {
+                const float mc = m_run[qb] * a.c;
+                float acc = 0.f;
 #pragma unroll
-            for (int kb = 0; kb < NKB; ++kb)
+                for (int kc = 0; kc < NKC; ++kc) {
+                    const f32x4 lo = sacc[qb][2 * kc], hi = sacc[qb][2 * kc + 1];
+                    half2 h[4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) mx = fmaxf(mx, sacc[qb][kb][e]);
-            mx = max_xor16(mx);
-            mx = max_xor32(mx);
-            const float m_new = fmaxf(m_run[qb], mx);
-            const float alpha = __builtin_amdgcn_exp2f((m_run[qb] - m_new) * a.c);
-            const float mc = m_new * a.c;
-            float rs = 0.f;
+                    for (int e = 0; e < 2; ++e) {
+                        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(lo[2 * e], a.c, -mc));
+                        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(lo[2 * e + 1], a.c, -mc));
+                        const float p2 = __builtin_amdgcn_exp2f(__builtin_fmaf(hi[2 * e], a.c, -mc));
+                        const float p3 = __builtin_amdgcn_exp2f(__builtin_fmaf(hi[2 * e + 1], a.c, -mc));
+                        h[e] = half2{(_Float16)p0, (_Float16)p1};
+                        h[2 + e] = half2{(_Float16)p2, (_Float16)p3};
+                    }
+                    // row sum over the fp16 probabilities actually fed to the PV product
 #pragma unroll
-            for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[qb][kb][e], a.c, -mc));
-                    sacc[qb][kb][e] = p;
-                    rs += p;
+                    for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_fdot2(h[e], kOnes2, acc, false);
+                    pb[qb][kc] = half8{h[0][0], h[0][1], h[1][0], h[1][1], h[2][0], h[2][1], h[3][0], h[3][1]};
                 }
-            l_run[qb] = l_run[qb] * alpha + rs;
-            m_run[qb] = m_new;
-#pragma unroll
-            for (int db = 0; db < DB; ++db) oacc[db][qb] *= alpha;
-#pragma unroll
-            for (int kc = 0; kc < NKC; ++kc) {
-                const f32x4 lo = sacc[qb][2 * kc], hi = sacc[qb][2 * kc + 1];
-                pb[qb][kc] = half8{(_Float16)lo[0], (_Float16)lo[1], (_Float16)lo[2], (_Float16)lo[3],
-                                   (_Float16)hi[0], (_Float16)hi[1], (_Float16)hi[2], (_Float16)hi[3]};
+                rs[qb] = acc;
             }
+        };
+        bool move_ref = (t == 0);
+        if (!move_ref) {
+            exponentiate();
+            bool over = false;
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) over |= !(rs[qb] < kSpeculateLimit);
+            move_ref = __builtin_amdgcn_ballot_w64(over) != 0;  // wave-uniform
         }
+        if (move_ref) {
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) {
+                float a0 = fmaxf(sacc[qb][0][0], sacc[qb][0][1]);
+                float a1 = fmaxf(sacc[qb][0][2], sacc[qb][0][3]);
+#pragma unroll
+                for (int kb = 1; kb < NKB; ++kb) {
+                    a0 = fmaxf(a0, fmaxf(sacc[qb][kb][0], sacc[qb][kb][1]));
+                    a1 = fmaxf(a1, fmaxf(sacc[qb][kb][2], sacc[qb][kb][3]));
+                }
+                const float mx = max_xor32(max_xor16(fmaxf(a0, a1)));
+                const float m_new = fmaxf(m_run[qb], mx);
+                const float alpha = __builtin_amdgcn_exp2f((m_run[qb] - m_new) * a.c);
+                m_run[qb] = m_new;
+                l_run[qb] *= alpha;
+#pragma unroll
+                for (int db = 0; db < DB; ++db) oacc[db][qb] *= alpha;
+            }
+            exponentiate();
+        }
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) l_run[qb] += rs[qb];
 
         // ---- O^T += V^T P^T on MFMA ----
         // Source lane l16 of group g points at row 4g + l16/4 (+16 for the second
         // half) and columns 16*db + 4*(l16%4) .. +3; the transposing read returns
         // V[32kc + 4g + e][16db + l16] in element e.
+        if (FA2_SETPRIO) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-            const int lc = 2 * db + ((l16 & 3) >> 1);
-            const int within = 4 * (l16 & 1);
 #pragma unroll
             for (int kc = 0; kc < NKC; ++kc) {
-                const int r0 = 32 * kc + 4 * g + (l16 >> 2);
-                const int r1 = r0 + 16;
-                const s16x4 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_s16x4*)(ldsV + r0 * D + 8 * (lc ^ swz_v<D>(r0)) + within));
-                const s16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_s16x4*)(ldsV + r1 * D + 8 * (lc ^ swz_v<D>(r1)) + within));
+                const char* p0 = ldsV + rdV[db] + kc * 32 * D * 2;
+                const s16x4 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p0);
+                const s16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0 + 16 * D * 2));
                 const half4 h0 = __builtin_bit_cast(half4, t0);
                 const half4 h1 = __builtin_bit_cast(half4, t1);
                 const half8 va = half8{h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
@@ -318,6 +446,14 @@ __global__ __launch_bounds__(SH::THREADS) void fa2_fwd_kernel(KernelArgs a) {
                     oacc[db][qb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb[qb][kc], oacc[db][qb], 0, 0, 0);
             }
         }
+        if (FA2_SETPRIO) __builtin_amdgcn_s_setprio(0);
+    };
+
+    // The ring stage alternates with the tile index; stepping two tiles per
+    // iteration makes it a compile-time constant, so LDS offsets are immediates.
+    for (int t = 0; t < n_tiles; t += 2) {
+        tile_step(t, Int<0>{});
+        if (t + 1 < n_tiles) tile_step(t + 1, Int<1>{});
     }
 
     // ---- epilogue: O = o / l in fp16, LSE = scale*m + ln(l) ----
@@ -341,8 +477,28 @@ __global__ __launch_bounds__(SH::THREADS) void fa2_fwd_kernel(KernelArgs a) {
     }
 }
 
-using Shape64 = Shape<64, 2, 4, 64>;
-using Shape128 = Shape<128, 2, 4, 64>;
+// Tile shapes per head dimension: <D, 16-query blocks per wave, waves, keys per tile>.
+// The defaults can be overridden at build time to compare tilings.
+#ifndef FA2_D64_QB
+#define FA2_D64_QB 2
+#endif
+#ifndef FA2_D64_NW
+#define FA2_D64_NW 8
+#endif
+#ifndef FA2_D64_BN
+#define FA2_D64_BN 64
+#endif
+#ifndef FA2_D128_QB
+#define FA2_D128_QB 2
+#endif
+#ifndef FA2_D128_NW
+#define FA2_D128_NW 8
+#endif
+#ifndef FA2_D128_BN
+#define FA2_D128_BN 64
+#endif
+using Shape64 = Shape<64, FA2_D64_QB, FA2_D64_NW, FA2_D64_BN>;
+using Shape128 = Shape<128, FA2_D128_QB, FA2_D128_NW, FA2_D128_BN>;
 
 template <class SH, bool CAUSAL>
 hipError_t launch_shape(const LaunchArgs& a, hipStream_t stream) {

@@ -84,7 +84,22 @@ def main():
     ap.add_argument("--causal", action="store_true", help="run the causal variant of the workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-stride", type=int, default=1, help="oracle sample: every n-th row (1 = all rows)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="instead of the benchmark, run 10 plain device-to-device copies of MIB MiB "
+                         "(the reference kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     args = ap.parse_args()
+
+    if args.copy_calibration:
+        import torch
+        n = args.copy_calibration * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(10):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": n * 4, "copy_calibration_bytes_written": n * 4,
+                          "copies": 10}), flush=True)
+        return
 
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: the forward pass here has no multi-GPU path "

@@ -144,6 +144,24 @@ def test_dominant_key():
         O, L = full_case(q, k, v, causal, 1.0, "dominant key")
 
 
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("direction", ["rising", "falling"])
+def test_monotone_scores(D, direction):
+    """Scores that grow (or shrink) by about 180 base-2 units per 64 keys: with
+    rising keys every key tile raises every row's maximum far beyond the
+    running one, so the running maximum and the rescale of the partial output
+    are exercised on every tile; with falling keys they never are."""
+    S = 515
+    q = np.zeros((1, 2, S, D), np.float16)
+    k = np.zeros((1, 2, S, D), np.float16)
+    q[..., 0] = 4.0
+    ramp = (np.arange(S) * 0.5).astype(np.float16)
+    k[0, :, :, 0] = ramp if direction == "rising" else ramp[::-1]
+    _, _, v = make_random(42_000 + D, 1, 2, S, D)
+    for causal in (False, True):
+        full_case(q, k, v, causal, 1.0, f"{direction} keys D={D}")
+
+
 def test_deterministic():
     q, k, v = make_random(50_000, 2, 3, 1000, 64, sigma_qk=3.0)
     for causal in (False, True):
