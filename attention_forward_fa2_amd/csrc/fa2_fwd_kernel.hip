@@ -129,7 +129,15 @@ __device__ __forceinline__ float sum_xor32(float x) {
 // the LDS base; nothing else in this kernel uses M0.
 //   dma_16B_s: address = 64-bit wave-uniform base (SGPRs) + 32-bit lane offset.
 //   dma_16B_v: full 64-bit per-lane address.
-__device__ __forceinline__ void dma_16B_s(const void* sbase, uint32_t voff, uint32_t lds_base) {
+__device__ __forceinline__ void dma_16B_s(const void* sbase_in, uint32_t voff, uint32_t lds_base) {
+    // The base is wave-uniform; say so, so it is kept in SGPRs as the
+    // instruction requires.
+    // (readfirstlane returns a signed int: go through uint32_t so the low half
+    // is zero-extended, not sign-extended, when it is widened.)
+    const uint64_t b = reinterpret_cast<uint64_t>(sbase_in);
+    const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+    const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+    const void* sbase = reinterpret_cast<const void*>((hi << 32) | lo);
     asm volatile(
         "s_mov_b32 m0, %2\n\t"
         "s_nop 0\n\t"
@@ -168,6 +176,36 @@ struct KernelArgs {
     float c;       // scale * log2(e)
 };
 
+// Workgroup -> (head bh, query tile qt). Consecutive workgroup ids are
+// dispatched round-robin to the 8 XCDs, each with its own L2, so the mapping
+// keeps the workgroups that read one head's K/V on one XCD:
+//  * non-causal: XCD x gets a contiguous run of (head, tile) pairs in head-major
+//    order, i.e. all query tiles of a few heads;
+//  * causal with B*H a multiple of 8: XCD x gets heads x, x+8, ..., and walks
+//    them heaviest query tile first (the last tiles see the most keys), so the
+//    long workgroups start early and each head has several tiles in flight on
+//    one XCD;
+//  * causal otherwise: heaviest tiles first over all heads.
+template <bool CAUSAL>
+__device__ __forceinline__ void map_block(const KernelArgs& a, int& bh, int& qt) {
+    const int bid = blockIdx.x, xcd = bid & 7, slot = bid >> 3;
+    if (CAUSAL && (a.BH & 7) == 0) {
+        const int hx = a.BH >> 3;  // heads per XCD
+        qt = a.nqt - 1 - slot / hx;
+        bh = xcd + 8 * (slot % hx);
+        return;
+    }
+    const int per = a.nblocks >> 3, rem = a.nblocks & 7;
+    const int logical = xcd * per + min(xcd, rem) + slot;
+    if (CAUSAL) {
+        qt = a.nqt - 1 - logical / a.BH;
+        bh = logical % a.BH;
+    } else {
+        bh = logical / a.nqt;
+        qt = logical % a.nqt;
+    }
+}
+
 // Raise the wave priority around the MFMA blocks so the arbiter keeps the matrix
 // unit fed from whichever wave has MFMAs ready (a scheduling hint only).
 #ifndef FA2_SETPRIO
@@ -190,20 +228,8 @@ void fa2_fwd_kernel(KernelArgs a) {
     const int l16 = lane & 15;
     const int g = lane >> 4;
 
-    // Workgroup -> (head, query tile). Consecutive workgroup ids go round-robin
-    // to the 8 XCDs; regroup them so each XCD gets a contiguous run of logical
-    // ids, which keeps the query tiles of one head (and its K/V in L2) together.
-    const int bid = blockIdx.x;
-    const int per = a.nblocks >> 3, rem = a.nblocks & 7, xcd = bid & 7;
-    const int logical = xcd * per + min(xcd, rem) + (bid >> 3);
     int bh, qt;
-    if (CAUSAL) {  // heaviest query tiles (most key tiles) first
-        qt = a.nqt - 1 - logical / a.BH;
-        bh = logical % a.BH;
-    } else {
-        bh = logical / a.nqt;
-        qt = logical % a.nqt;
-    }
+    map_block<CAUSAL>(a, bh, qt);
 
     const int S = a.S;
     const long long head = (long long)bh * S * D;
