@@ -64,12 +64,14 @@ constexpr float kMaxInit = -1.0e30f;
 // them overflowed fp16 (largest finite 65504).
 constexpr float kSpeculateLimit = 32768.0f;
 
-template <int D_, int QB_, int NW_, int BN_>
+template <int D_, int QB_, int NW_, int BN_, int SUB_>
 struct Shape {
     static constexpr int D = D_;
     static constexpr int QB = QB_;            // 16-query blocks per wave
     static constexpr int NW = NW_;            // waves per workgroup
-    static constexpr int BN = BN_;            // keys per tile
+    static constexpr int BN = BN_;            // keys per compute tile
+    static constexpr int SUB = SUB_;          // compute tiles per LDS ring stage
+    static constexpr int KB = SUB * BN;       // keys per ring stage (one barrier each)
     static constexpr int QW = 16 * QB;        // query rows per wave
     static constexpr int BM = NW * QW;        // query rows per workgroup
     static constexpr int THREADS = 64 * NW;
@@ -78,13 +80,15 @@ struct Shape {
     static constexpr int DK = D / 32;         // k-steps of one score MFMA block
     static constexpr int DB = D / 16;         // 16-wide column blocks of the output
     static constexpr int CPR = D / 8;         // 16-byte chunks per row
-    static constexpr int TILE = BN * D;       // halves per K or V tile
-    static constexpr int LOADS = TILE / 8 / 64 / NW;  // 16-byte loads per lane per tensor per tile
-    static constexpr int LDS_BYTES = 2 /*stages*/ * 2 /*K,V*/ * TILE * 2;
+    static constexpr int TILE = BN * D;       // halves per K or V compute tile
+    static constexpr int LTILE = SUB * TILE;  // halves per K or V ring stage
+    static constexpr int LOADS = LTILE / 8 / 64 / NW;  // 16-byte loads per lane per tensor per stage
+    static constexpr int LDS_BYTES = 2 /*stages*/ * 2 /*K,V*/ * LTILE * 2;
     // Occupancy the register allocation targets (waves per SIMD).
     static constexpr int WAVES_PER_SIMD = (D == 64 && QB <= 2) ? 4 : (QB <= 2 ? 2 : 1);
     static_assert(BN % 32 == 0 && D % 32 == 0, "tile shape");
-    static_assert((TILE / 8) % (64 * NW) == 0, "loads must divide evenly among lanes");
+    static_assert((LTILE / 8) % (64 * NW) == 0, "loads must divide evenly among lanes");
+    static_assert(BN % 16 == 0, "swizzles repeat every 16 rows, so sub-tiles share them");
 };
 
 // XOR swizzles of the 16-byte chunk index within a row, chosen so that the 16
@@ -217,9 +221,9 @@ __global__ __launch_bounds__(SH::THREADS) __attribute__((amdgpu_waves_per_eu(SH:
 void fa2_fwd_kernel(KernelArgs a) {
     constexpr int D = SH::D, QB = SH::QB, NW = SH::NW, BN = SH::BN, QW = SH::QW, BM = SH::BM;
     constexpr int NKB = SH::NKB, NKC = SH::NKC, DK = SH::DK, DB = SH::DB, CPR = SH::CPR;
-    constexpr int TILE = SH::TILE, LOADS = SH::LOADS;
+    constexpr int TILE = SH::TILE, LTILE = SH::LTILE, LOADS = SH::LOADS, SUB = SH::SUB, KB = SH::KB;
 
-    // LDS ring: [stage][K | V][TILE] halves.
+    // LDS ring: [stage][K | V][LTILE] halves; a stage holds SUB compute tiles.
     extern __shared__ __attribute__((aligned(16))) _Float16 smem[];
     const uint32_t lds_base = __builtin_amdgcn_readfirstlane(lds_addr(smem));
 
@@ -239,46 +243,45 @@ void fa2_fwd_kernel(KernelArgs a) {
     const int q0 = qt * BM;
     const int qw0 = q0 + wave * QW;
 
-    int n_tiles = (S + BN - 1) / BN;
-    if (CAUSAL) n_tiles = min(n_tiles, (min(q0 + BM, S) - 1) / BN + 1);
+    // Ring stages to scan (each KB keys).
+    int n_tiles = (S + KB - 1) / KB;
+    if (CAUSAL) n_tiles = min(n_tiles, (min(q0 + BM, S) - 1) / KB + 1);
 
-    // Per-lane source offsets (bytes, within a tile) of this lane's direct-to-LDS
-    // loads: load i fills LDS chunk c = (i*NW + wave)*64 + lane, i.e. tile row
-    // r = c / CPR and physical chunk pc = c % CPR, from the logical chunk
-    // pc ^ swz(r) of key row k0 + r. Loop-invariant; the tile base is scalar.
-    uint32_t offK[LOADS], offV[LOADS];
-    int rowL[LOADS];
-#pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-        const int c = (i * NW + wave) * 64 + lane;
-        const int r = c / CPR, pc = c % CPR;
-        rowL[i] = r;
-        offK[i] = 2u * (r * D + 8 * (pc ^ swz_k<D>(r)));
-        offV[i] = 2u * (r * D + 8 * (pc ^ swz_v<D>(r)));
-    }
+    // Per-lane source offsets (bytes, within a stage) of this lane's
+    // direct-to-LDS loads: load i fills LDS chunk c = (i*NW + wave)*64 + lane,
+    // i.e. stage row r = c / CPR and physical chunk pc = c % CPR, from the
+    // logical chunk pc ^ swz(r) of key row k0 + r. Successive loads of a lane are
+    // ROWS_PER_LOAD rows apart, a multiple of the 16-row swizzle period, so one
+    // lane offset per tensor serves all of them; the rest is a scalar step.
+    constexpr int ROWS_PER_LOAD = NW * 64 / CPR;
+    static_assert(ROWS_PER_LOAD % 16 == 0, "loads of a lane must keep the swizzle phase");
+    const int row0 = (wave * 64 + lane) / CPR;
+    const int pc0 = lane % CPR;
+    const uint32_t offK = 2u * (row0 * D + 8 * (pc0 ^ swz_k<D>(row0)));
+    const uint32_t offV = 2u * (row0 * D + 8 * (pc0 ^ swz_v<D>(row0)));
 
-    // Issue the direct-to-LDS loads of K/V tile t into ring stage ST. Rows past
-    // the end of the sequence (only in the last tile) are clamped to row S-1;
-    // their scores are masked to -inf before use.
+    // Issue the direct-to-LDS loads of K/V stage t (keys t*KB ..) into ring stage
+    // ST. Rows past the end of the sequence (only in the last stage) are clamped
+    // to row S-1; their scores are masked to -inf before use.
     auto issue_tile = [&](int t, auto st_c) {
         constexpr int ST = decltype(st_c)::value;
-        const int k0 = t * BN;
-        if (k0 + BN <= S) {
-            const _Float16* kt = Kh + (long long)k0 * D;
-            const _Float16* vt = Vh + (long long)k0 * D;
+        const int k0 = t * KB;
+        if (k0 + KB <= S) {
 #pragma unroll
             for (int i = 0; i < LOADS; ++i) {
+                const long long rows = (long long)k0 + i * ROWS_PER_LOAD;
                 const uint32_t dst = lds_base + 2u * (i * NW + wave) * 512;
-                dma_16B_s(kt, offK[i], dst + 2u * (ST * 2 + 0) * TILE);
-                dma_16B_s(vt, offV[i], dst + 2u * (ST * 2 + 1) * TILE);
+                dma_16B_s(Kh + rows * D, offK, dst + 2u * (ST * 2 + 0) * LTILE);
+                dma_16B_s(Vh + rows * D, offV, dst + 2u * (ST * 2 + 1) * LTILE);
             }
         } else {
 #pragma unroll
             for (int i = 0; i < LOADS; ++i) {
+                const int r = row0 + i * ROWS_PER_LOAD;
+                const long long shift = (long long)(min(k0 + r, S - 1) - row0) * D;
                 const uint32_t dst = lds_base + 2u * (i * NW + wave) * 512;
-                const long long shift = (long long)(min(k0 + rowL[i], S - 1) - rowL[i]) * D;
-                dma_16B_v((const char*)(Kh + shift) + offK[i], dst + 2u * (ST * 2 + 0) * TILE);
-                dma_16B_v((const char*)(Vh + shift) + offV[i], dst + 2u * (ST * 2 + 1) * TILE);
+                dma_16B_v((const char*)(Kh + shift) + offK, dst + 2u * (ST * 2 + 0) * LTILE);
+                dma_16B_v((const char*)(Vh + shift) + offV, dst + 2u * (ST * 2 + 1) * LTILE);
             }
         }
     };
@@ -330,21 +333,9 @@ void fa2_fwd_kernel(KernelArgs a) {
         }
     }
 
-    // One step of the scan over key tile t held in ring stage ST.
-    auto tile_step = [&](int t, auto st_c) {
-        constexpr int ST = decltype(st_c)::value;
-        // Tile t is resident for every wave (each waits for its own loads, then
-        // the barrier), and every wave has finished reading the other stage
-        // (tile t-1), which the next loads overwrite.
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-        if (t + 1 < n_tiles) issue_tile(t + 1, Int<1 - ST>{});
-
-        const int k0 = t * BN;
-        if (CAUSAL && k0 > qw0 + QW - 1) return;  // tile lies above this wave's diagonal
-
-        const char* const ldsK = reinterpret_cast<const char*>(smem) + 2 * (ST * 2 + 0) * TILE;
-        const char* const ldsV = reinterpret_cast<const char*>(smem) + 2 * (ST * 2 + 1) * TILE;
+    // One compute tile: keys k0 .. k0+BN-1, K and V at the given LDS addresses.
+    auto compute_tile = [&](const int k0, const char* const ldsK, const char* const ldsV)
+                            __attribute__((always_inline)) {
 
         // ---- S^T = K Q^T on MFMA ----
         if (FA2_SETPRIO) __builtin_amdgcn_s_setprio(1);
@@ -421,7 +412,7 @@ void fa2_fwd_kernel(KernelArgs a) {
                 rs[qb] = acc;
             }
         };
-        bool move_ref = (t == 0);
+        bool move_ref = (k0 == 0);
         if (!move_ref) {
             exponentiate();
             bool over = false;
@@ -475,6 +466,25 @@ void fa2_fwd_kernel(KernelArgs a) {
         if (FA2_SETPRIO) __builtin_amdgcn_s_setprio(0);
     };
 
+    // One step of the scan over ring stage t (SUB compute tiles) held in stage ST.
+    auto tile_step = [&](int t, auto st_c) {
+        constexpr int ST = decltype(st_c)::value;
+        // Stage t is resident for every wave (each waits for its own loads, then
+        // the barrier), and every wave has finished reading the other stage
+        // (stage t-1), which the next loads overwrite.
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (t + 1 < n_tiles) issue_tile(t + 1, Int<1 - ST>{});
+#pragma unroll
+        for (int j = 0; j < SUB; ++j) {
+            const int k0 = t * KB + j * BN;
+            if (k0 >= S) break;                         // past the end (last stage only)
+            if (CAUSAL && k0 > qw0 + QW - 1) break;     // above this wave's diagonal
+            compute_tile(k0, reinterpret_cast<const char*>(smem) + 2 * ((ST * 2 + 0) * LTILE + j * TILE),
+                         reinterpret_cast<const char*>(smem) + 2 * ((ST * 2 + 1) * LTILE + j * TILE));
+        }
+    };
+
     // The ring stage alternates with the tile index; stepping two tiles per
     // iteration makes it a compile-time constant, so LDS offsets are immediates.
     for (int t = 0; t < n_tiles; t += 2) {
@@ -523,8 +533,14 @@ void fa2_fwd_kernel(KernelArgs a) {
 #ifndef FA2_D128_BN
 #define FA2_D128_BN 64
 #endif
-using Shape64 = Shape<64, FA2_D64_QB, FA2_D64_NW, FA2_D64_BN>;
-using Shape128 = Shape<128, FA2_D128_QB, FA2_D128_NW, FA2_D128_BN>;
+#ifndef FA2_D64_SUB
+#define FA2_D64_SUB 2
+#endif
+#ifndef FA2_D128_SUB
+#define FA2_D128_SUB 2
+#endif
+using Shape64 = Shape<64, FA2_D64_QB, FA2_D64_NW, FA2_D64_BN, FA2_D64_SUB>;
+using Shape128 = Shape<128, FA2_D128_QB, FA2_D128_NW, FA2_D128_BN, FA2_D128_SUB>;
 
 template <class SH, bool CAUSAL>
 hipError_t launch_shape(const LaunchArgs& a, hipStream_t stream) {
@@ -556,8 +572,8 @@ hipError_t launch_shape(const LaunchArgs& a, hipStream_t stream) {
 }  // namespace
 
 TileShape tile_shape(int D, int /*causal*/) {
-    if (D == 128) return {Shape128::BM, Shape128::BN, Shape128::THREADS, Shape128::LDS_BYTES};
-    return {Shape64::BM, Shape64::BN, Shape64::THREADS, Shape64::LDS_BYTES};
+    if (D == 128) return {Shape128::BM, Shape128::KB, Shape128::THREADS, Shape128::LDS_BYTES};
+    return {Shape64::BM, Shape64::KB, Shape64::THREADS, Shape64::LDS_BYTES};
 }
 
 hipError_t launch_forward(const LaunchArgs& a, hipStream_t stream) {

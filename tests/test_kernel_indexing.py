@@ -26,7 +26,9 @@ def swz_v(D, r):
     return (((r >> 1) & 3) << 1) if D == 64 else ((r & 7) << 1)
 
 
-SHAPES = {64: (2, 8, 64), 128: (2, 8, 64)}  # D -> (QB, NW, BN) of the library's tiles
+# D -> (QB, NW, BN, SUB) of the library's tiles (SUB compute tiles per LDS stage)
+SHAPES = {64: (2, 8, 64, 2), 128: (2, 8, 64, 2)}
+VARIANTS = [(2, 8, 64, 1), (2, 8, 64, 2), (2, 4, 64, 1), (2, 4, 64, 2), (4, 4, 64, 1)]
 
 
 def block_map(BH, nqt, causal):
@@ -52,11 +54,14 @@ def test_block_mapping_is_a_bijection(BH, nqt, causal):
     assert len(set(zip(bh.tolist(), qt.tolist()))) == BH * nqt
 
 
-def emulate(B, H, S, D, causal):
-    QB, NW, BN = SHAPES[D]
+def emulate(B, H, S, D, causal, shape=None):
+    QB, NW, BN, SUB = shape or SHAPES[D]
     QW, BM = 16 * QB, 16 * QB * NW
     CPR, TILE, DB, NKC, NKB, DK = D // 8, BN * D, D // 16, BN // 32, BN // 16, D // 32
-    LOADS = TILE // 8 // 64 // NW
+    KB, LTILE = SUB * BN, SUB * BN * D
+    LOADS = LTILE // 8 // 64 // NW
+    RPL = NW * 64 // CPR
+    assert RPL % 16 == 0
     lane = np.arange(64)
     l16, g = lane & 15, lane >> 4
     nqt = -(-S // BM)
@@ -70,22 +75,27 @@ def emulate(B, H, S, D, causal):
             for kk in range(DK):
                 off = bh[:, None] * S * D + row * D + 32 * kk + 8 * g[None, :]
                 assert off.min() >= 0 and (off + 8).max() <= total
-        # K/V direct-to-LDS loads
+        # K/V direct-to-LDS loads: the kernel keeps one lane offset (row0, pc0)
+        # per tensor and steps the scalar base by RPL rows per load
+        row0, pc0 = (wave * 64 + lane) // CPR, lane % CPR
         for i in range(LOADS):
             c = (i * NW + wave) * 64 + lane
             r, pc = c // CPR, c % CPR
+            assert np.array_equal(r, row0 + i * RPL) and np.array_equal(pc, pc0)
             dst = 2 * (i * NW + wave) * 512 + 16 * lane
-            assert dst.min() >= 0 and (dst + 16).max() <= 2 * TILE
+            assert dst.min() >= 0 and (dst + 16).max() <= 2 * LTILE
             for sw in (swz_k, swz_v):
-                off = r * D + 8 * (pc ^ sw(D, r))
-                for t in range(-(-S // BN)):
-                    k0 = t * BN
-                    if k0 + BN <= S:
-                        el = k0 * D + off
+                generic = r * D + 8 * (pc ^ sw(D, r))
+                lane_off = row0 * D + 8 * (pc0 ^ sw(D, row0))
+                assert np.array_equal(generic, lane_off + i * RPL * D)
+                for t in range(-(-S // KB)):
+                    k0 = t * KB
+                    if k0 + KB <= S:
+                        el = (k0 + i * RPL) * D + lane_off
                     else:
-                        el = (np.minimum(k0 + r, S - 1) - r) * D + off
+                        el = (np.minimum(k0 + r, S - 1) - row0) * D + lane_off
                         ok = k0 + r < S
-                        assert np.array_equal(el[ok], (k0 * D + off)[ok])
+                        assert np.array_equal(el[ok], (k0 * D + generic)[ok])
                     assert el.min() >= 0 and (el + 8).max() <= S * D
         # O and LSE stores
         for qb in range(QB):
@@ -108,9 +118,17 @@ def test_global_accesses_in_bounds(D, S, causal):
     emulate(2, 4, S, D, causal)
 
 
+@pytest.mark.parametrize("shape", VARIANTS, ids=[f"QB{a}NW{b}BN{c}SUB{d}" for a, b, c, d in VARIANTS])
+@pytest.mark.parametrize("D", [64, 128])
+def test_global_accesses_in_bounds_other_tilings(shape, D):
+    for S in (1, 63, 65, 129, 257, 1000):
+        for causal in (False, True):
+            emulate(2, 3, S, D, causal, shape)
+
+
 @pytest.mark.parametrize("D", [64, 128])
 def test_lds_reads_and_bank_groups(D):
-    QB, NW, BN = SHAPES[D]
+    QB, NW, BN, SUB = SHAPES[D]
     TILE, DB, NKC, NKB, DK = BN * D, D // 16, BN // 32, BN // 16, D // 32
     lane = np.arange(64)
     l16, g = lane & 15, lane >> 4
@@ -156,7 +174,7 @@ def test_transposing_reads_match_the_score_layout(D):
     """The V^T operand must list, for lane (d = 16db + lane%16, g = lane/16),
     the keys 32kc + 4g + e (first read) and 32kc + 16 + 4g + e (second read):
     the keys the S^T accumulator of that lane holds (16-key blocks 2kc, 2kc+1)."""
-    BN = SHAPES[D][2]
+    BN = SHAPES[D][2] * 2  # two compute tiles: a sub-tile starts at a multiple of BN rows
     # LDS tile as the DMA writes it: row r, physical chunk pc holds logical chunk pc ^ swz_v(r)
     key_of = np.zeros(BN * D, dtype=np.int64)
     col_of = np.zeros(BN * D, dtype=np.int64)
@@ -172,7 +190,7 @@ def test_transposing_reads_match_the_score_layout(D):
     for db in range(D // 16):
         lc = 2 * db + ((l16 & 3) >> 1)
         base = r0 * D + 8 * (lc ^ swz_v(D, r0)) + 4 * (l16 & 1)
-        for kc in range(BN // 32):
+        for kc in range(BN // 32):  # key chunks of both sub-tiles
             for half in (0, 1):
                 a = base + kc * 32 * D + half * 16 * D
                 keys, cols = tr16(a, key_of), tr16(a, col_of)
