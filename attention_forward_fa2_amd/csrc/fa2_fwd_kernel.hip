@@ -40,6 +40,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+#include <cmath>
 #include <type_traits>
 
 #include "fa2_internal.h"
@@ -167,41 +169,64 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 template <int V>
 using Int = std::integral_constant<int, V>;
 
+// Everything the kernel needs about one launch. Tensors are addressed through
+// element strides so that one kernel serves the dense [B,H,S,D] layout and the
+// packed variable-length layout [total,H,D]:
+//   element (b, h, row, d) of q/o at  q + b*q_sb + h*q_sh + (start_b + row)*q_sr + d
+//   element (b, hk, row, d) of k/v at k + b*kv_sb + hk*kv_sh + (start_b + row)*kv_sr + d
+//   lse (b, h, row)                at  lse + b*l_sb + h*l_sh + start_b + row
+// where start_b = cu[b] and the sequence length len_b = cu[b+1] - cu[b] when a
+// sequence table cu is given, and start_b = 0, len_b = S otherwise.
 struct KernelArgs {
     const _Float16* q;
     const _Float16* k;
     const _Float16* v;
     _Float16* o;
     float* lse;
-    int S;
-    int BH;        // B*H
-    int nqt;       // query tiles per head
-    int nblocks;   // BH * nqt
-    float c;       // scale * log2(e)
+    const int* cu;        // [nseq+1] start rows of packed sequences, or null
+    long long q_sb, q_sh, kv_sb, kv_sh, l_sb, l_sh;
+    int q_sr, kv_sr;
+    int S;                // sequence length (dense) or longest sequence (packed)
+    int total;            // rows of the packed tensors (packed only)
+    int H;                // query heads
+    int group;            // query heads per K/V head (H / H_kv)
+    int BH;               // sequences * H
+    int BHkv;             // sequences * H_kv
+    int nqt;              // query tiles per (sequence, head)
+    int nblocks;          // BH * nqt
+    int wl, wr;           // local window: keys i-wl .. i+wr (window kernels only)
+    float c;              // scale * log2(e)
+    float out_scale;      // 1/(1-p) with dropout, else 1
+    uint32_t drop_thr;    // a key is kept when its 32-bit draw is >= drop_thr
+    uint32_t seed_lo, seed_hi, offset;
 };
 
-// Workgroup -> (head bh, query tile qt). Consecutive workgroup ids are
+enum MaskKind { kNoMask = 0, kCausal = 1, kWindow = 2 };
+
+// Workgroup -> (sequence*H + head, query tile). Consecutive workgroup ids are
 // dispatched round-robin to the 8 XCDs, each with its own L2, so the mapping
-// keeps the workgroups that read one head's K/V on one XCD:
-//  * non-causal: XCD x gets a contiguous run of (head, tile) pairs in head-major
-//    order, i.e. all query tiles of a few heads;
-//  * causal with B*H a multiple of 8: XCD x gets heads x, x+8, ..., and walks
-//    them heaviest query tile first (the last tiles see the most keys), so the
-//    long workgroups start early and each head has several tiles in flight on
-//    one XCD;
+// keeps the workgroups that read one K/V head on one XCD:
+//  * non-causal and windowed: XCD x gets a contiguous run of (head, tile) pairs
+//    in head-major order, i.e. all query tiles of a few heads; heads that share
+//    a K/V head are adjacent;
+//  * causal with (sequences * K/V heads) a multiple of 8: XCD x gets K/V heads
+//    x, x+8, ... with all query heads of each, and walks them heaviest query
+//    tile first (the last tiles see the most keys), so the long workgroups
+//    start early and each K/V head has several tiles in flight on one XCD;
 //  * causal otherwise: heaviest tiles first over all heads.
-template <bool CAUSAL>
-__device__ __forceinline__ void map_block(const KernelArgs& a, int& bh, int& qt) {
-    const int bid = blockIdx.x, xcd = bid & 7, slot = bid >> 3;
-    if (CAUSAL && (a.BH & 7) == 0) {
-        const int hx = a.BH >> 3;  // heads per XCD
-        qt = a.nqt - 1 - slot / hx;
-        bh = xcd + 8 * (slot % hx);
+template <int MASK>
+__device__ __forceinline__ void map_block(const KernelArgs& a, int bid, int& bh, int& qt) {
+    const int xcd = bid & 7, slot = bid >> 3;
+    if (MASK == kCausal && (a.BHkv & 7) == 0) {
+        const int per_tile = (a.BHkv >> 3) * a.group;  // query heads per XCD
+        qt = a.nqt - 1 - slot / per_tile;
+        const int r = slot % per_tile;
+        bh = (xcd + 8 * (r / a.group)) * a.group + r % a.group;
         return;
     }
     const int per = a.nblocks >> 3, rem = a.nblocks & 7;
     const int logical = xcd * per + min(xcd, rem) + slot;
-    if (CAUSAL) {
+    if (MASK == kCausal) {
         qt = a.nqt - 1 - logical / a.BH;
         bh = logical % a.BH;
     } else {
@@ -210,13 +235,38 @@ __device__ __forceinline__ void map_block(const KernelArgs& a, int& bh, int& qt)
     }
 }
 
+// Philox4x32-10 (Salmon, Moraes, Dror and Shaw, "Parallel random numbers: as
+// easy as 1, 2, 3", SC 2011): ten rounds of two 32x32->64-bit products and xors
+// on a 4-word counter under a 2-word key that advances by the Weyl constants
+// between rounds. Returns the four output words.
+struct U32x4 {
+    uint32_t w[4];
+};
+__device__ __forceinline__ U32x4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3, uint32_t k0,
+                                               uint32_t k1) {
+#pragma unroll
+    for (int r = 0; r < 10; ++r) {
+        const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
+        const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
+        const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+        const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+        c1 = (uint32_t)p1;
+        c3 = (uint32_t)p0;
+        c0 = n0;
+        c2 = n2;
+        k0 += 0x9E3779B9u;
+        k1 += 0xBB67AE85u;
+    }
+    return U32x4{{c0, c1, c2, c3}};
+}
+
 // Raise the wave priority around the MFMA blocks so the arbiter keeps the matrix
 // unit fed from whichever wave has MFMAs ready (a scheduling hint only).
 #ifndef FA2_SETPRIO
 #define FA2_SETPRIO 1
 #endif
 
-template <class SH, bool CAUSAL>
+template <class SH, int MASK, bool DROP>
 __global__ __launch_bounds__(SH::THREADS) __attribute__((amdgpu_waves_per_eu(SH::WAVES_PER_SIMD)))
 void fa2_fwd_kernel(KernelArgs a) {
     constexpr int D = SH::D, QB = SH::QB, NW = SH::NW, BN = SH::BN, QW = SH::QW, BM = SH::BM;
@@ -232,20 +282,42 @@ void fa2_fwd_kernel(KernelArgs a) {
     const int l16 = lane & 15;
     const int g = lane >> 4;
 
+    const int bid = blockIdx.x + blockIdx.y * gridDim.x;  // grid is (x, y) only when x alone is too small
+    if (bid >= a.nblocks) return;
     int bh, qt;
-    map_block<CAUSAL>(a, bh, qt);
+    map_block<MASK>(a, bid, bh, qt);
+    const int b = bh / a.H, h = bh - b * a.H, hk = h / a.group;
 
-    const int S = a.S;
-    const long long head = (long long)bh * S * D;
-    const _Float16* __restrict__ Qh = a.q + head;
-    const _Float16* __restrict__ Kh = a.k + head;
-    const _Float16* __restrict__ Vh = a.v + head;
+    // This sequence's first row and length. A packed table is read with scalar
+    // loads and clamped to the tensors, so a malformed table cannot make the
+    // kernel address memory outside them.
+    int start = 0, len = a.S;
+    if (a.cu) {
+        const int s0 = min(max(a.cu[b], 0), a.total);
+        const int s1 = min(max(a.cu[b + 1], s0), a.total);
+        start = s0;
+        len = min(s1 - s0, a.S);
+    }
     const int q0 = qt * BM;
+    if (q0 >= len) return;  // whole workgroup: no barrier has been reached
     const int qw0 = q0 + wave * QW;
+    const int q_sr = a.q_sr, kv_sr = a.kv_sr;
 
-    // Ring stages to scan (each KB keys).
-    int n_tiles = (S + KB - 1) / KB;
-    if (CAUSAL) n_tiles = min(n_tiles, (min(q0 + BM, S) - 1) / KB + 1);
+    const _Float16* __restrict__ Qh = a.q + b * a.q_sb + h * a.q_sh + (long long)start * q_sr;
+    const _Float16* __restrict__ Kh = a.k + b * a.kv_sb + hk * a.kv_sh + (long long)start * kv_sr;
+    const _Float16* __restrict__ Vh = a.v + b * a.kv_sb + hk * a.kv_sh + (long long)start * kv_sr;
+
+    // Keys this workgroup may need, [kbeg, kend), and the ring stages (KB keys
+    // each) that hold them.
+    const int q_last = min(q0 + BM, len) - 1;
+    int kbeg = 0, kend = len;
+    if (MASK == kCausal) kend = q_last + 1;
+    if (MASK == kWindow) {
+        kbeg = max(0, q0 - a.wl);
+        kend = min(len, q_last + a.wr + 1);
+    }
+    const int t_begin = kbeg / KB;
+    const int t_end = (kend + KB - 1) / KB;
 
     // Per-lane source offsets (bytes, within a stage) of this lane's
     // direct-to-LDS loads: load i fills LDS chunk c = (i*NW + wave)*64 + lane,
@@ -257,28 +329,28 @@ void fa2_fwd_kernel(KernelArgs a) {
     static_assert(ROWS_PER_LOAD % 16 == 0, "loads of a lane must keep the swizzle phase");
     const int row0 = (wave * 64 + lane) / CPR;
     const int pc0 = lane % CPR;
-    const uint32_t offK = 2u * (row0 * D + 8 * (pc0 ^ swz_k<D>(row0)));
-    const uint32_t offV = 2u * (row0 * D + 8 * (pc0 ^ swz_v<D>(row0)));
+    const uint32_t offK = 2u * (row0 * kv_sr + 8 * (pc0 ^ swz_k<D>(row0)));
+    const uint32_t offV = 2u * (row0 * kv_sr + 8 * (pc0 ^ swz_v<D>(row0)));
 
     // Issue the direct-to-LDS loads of K/V stage t (keys t*KB ..) into ring stage
     // ST. Rows past the end of the sequence (only in the last stage) are clamped
-    // to row S-1; their scores are masked to -inf before use.
+    // to row len-1; their scores are masked to -inf before use.
     auto issue_tile = [&](int t, auto st_c) {
         constexpr int ST = decltype(st_c)::value;
         const int k0 = t * KB;
-        if (k0 + KB <= S) {
+        if (k0 + KB <= len) {
 #pragma unroll
             for (int i = 0; i < LOADS; ++i) {
                 const long long rows = (long long)k0 + i * ROWS_PER_LOAD;
                 const uint32_t dst = lds_base + 2u * (i * NW + wave) * 512;
-                dma_16B_s(Kh + rows * D, offK, dst + 2u * (ST * 2 + 0) * LTILE);
-                dma_16B_s(Vh + rows * D, offV, dst + 2u * (ST * 2 + 1) * LTILE);
+                dma_16B_s(Kh + rows * kv_sr, offK, dst + 2u * (ST * 2 + 0) * LTILE);
+                dma_16B_s(Vh + rows * kv_sr, offV, dst + 2u * (ST * 2 + 1) * LTILE);
             }
         } else {
 #pragma unroll
             for (int i = 0; i < LOADS; ++i) {
                 const int r = row0 + i * ROWS_PER_LOAD;
-                const long long shift = (long long)(min(k0 + r, S - 1) - row0) * D;
+                const long long shift = (long long)(min(k0 + r, len - 1) - row0) * kv_sr;
                 const uint32_t dst = lds_base + 2u * (i * NW + wave) * 512;
                 dma_16B_v((const char*)(Kh + shift) + offK, dst + 2u * (ST * 2 + 0) * LTILE);
                 dma_16B_v((const char*)(Vh + shift) + offV, dst + 2u * (ST * 2 + 1) * LTILE);
@@ -286,17 +358,17 @@ void fa2_fwd_kernel(KernelArgs a) {
         }
     };
 
-    issue_tile(0, Int<0>{});
+    issue_tile(t_begin, Int<0>{});
 
     // Q^T as the B operand of the score MFMA, kept in registers for the whole scan.
     // Rows past the end are clamped (their results are never stored).
     half8 qreg[QB][DK];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-        const int row = min(qw0 + 16 * qb + l16, S - 1);
+        const int row = min(qw0 + 16 * qb + l16, len - 1);
 #pragma unroll
         for (int kk = 0; kk < DK; ++kk)
-            qreg[qb][kk] = *reinterpret_cast<const half8*>(Qh + (long long)row * D + 32 * kk + 8 * g);
+            qreg[qb][kk] = *reinterpret_cast<const half8*>(Qh + (long long)row * q_sr + 32 * kk + 8 * g);
     }
     // Wait for Q here with the compiler-visible s_waitcnt (vmcnt(0), expcnt and
     // lgkmcnt unconstrained): otherwise the compiler's wait for Q sits at its
@@ -316,6 +388,7 @@ void fa2_fwd_kernel(KernelArgs a) {
         l_run[qb] = 0.f;
     }
     const half2 kOnes2 = half2{(_Float16)1.0f, (_Float16)1.0f};
+    bool fresh = true;  // no tile computed by this wave yet
 
     // LDS read offsets (bytes) that do not depend on the tile: the K swizzle of
     // rows 16*kb + l16 depends on l16 only, the V swizzle of rows
@@ -356,8 +429,11 @@ void fa2_fwd_kernel(KernelArgs a) {
         }
         if (FA2_SETPRIO) __builtin_amdgcn_s_setprio(0);
 
-        // ---- masks: keys past the end, and keys after the query when causal ----
-        const bool need_mask = (k0 + BN > S) || (CAUSAL && k0 + BN - 1 > qw0);
+        // ---- masks: keys past the end, after the query (causal), outside the
+        // window (local) ----
+        bool need_mask = k0 + BN > len;
+        if (MASK == kCausal) need_mask |= k0 + BN - 1 > qw0;
+        if (MASK == kWindow) need_mask |= (k0 < qw0 + QW - 1 - a.wl) || (k0 + BN - 1 > qw0 + a.wr);
         if (need_mask) {
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb) {
@@ -367,7 +443,10 @@ void fa2_fwd_kernel(KernelArgs a) {
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int key = k0 + 16 * kb + 4 * g + e;
-                        if (key >= S || (CAUSAL && key > qrow)) sacc[qb][kb][e] = -INFINITY;
+                        bool out = key >= len;
+                        if (MASK == kCausal) out |= key > qrow;
+                        if (MASK == kWindow) out |= (key < qrow - a.wl) || (key > qrow + a.wr);
+                        if (out) sacc[qb][kb][e] = -INFINITY;
                     }
             }
         }
@@ -404,7 +483,8 @@ void fa2_fwd_kernel(KernelArgs a) {
                         h[e] = half2{(_Float16)p0, (_Float16)p1};
                         h[2 + e] = half2{(_Float16)p2, (_Float16)p3};
                     }
-                    // row sum over the fp16 probabilities actually fed to the PV product
+                    // row sum over the fp16 probabilities (before dropout: the
+                    // softmax normaliser counts every admissible key)
 #pragma unroll
                     for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_fdot2(h[e], kOnes2, acc, false);
                     pb[qb][kc] = half8{h[0][0], h[0][1], h[1][0], h[1][1], h[2][0], h[2][1], h[3][0], h[3][1]};
@@ -412,7 +492,7 @@ void fa2_fwd_kernel(KernelArgs a) {
                 rs[qb] = acc;
             }
         };
-        bool move_ref = (k0 == 0);
+        bool move_ref = fresh;
         if (!move_ref) {
             exponentiate();
             bool over = false;
@@ -440,8 +520,40 @@ void fa2_fwd_kernel(KernelArgs a) {
             }
             exponentiate();
         }
+        fresh = false;
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) l_run[qb] += rs[qb];
+
+        // ---- dropout on P: zero the probabilities of dropped keys ----
+        // Key j of query row i (both within the sequence) of head (b, h) draws
+        // word j%4 of Philox4x32-10 at counter (j/4, i, b*H + h, offset) under
+        // key (seed_lo, seed_hi), and is kept when that word is >= drop_thr. A
+        // lane's 4 keys of a 16-key block are 4 consecutive keys starting at a
+        // multiple of 4, i.e. one Philox call. Kept probabilities are scaled by
+        // 1/(1-p) in the epilogue.
+        if (DROP) {
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) {
+                const uint32_t qrow = (uint32_t)(qw0 + 16 * qb + l16);
+#pragma unroll
+                for (int kc = 0; kc < NKC; ++kc) {
+                    uint32_t m[4];
+#pragma unroll
+                    for (int half_ = 0; half_ < 2; ++half_) {
+                        const uint32_t jg = (uint32_t)((k0 + 32 * kc + 16 * half_) >> 2) + (uint32_t)g;
+                        const U32x4 r = philox4x32_10(jg, qrow, (uint32_t)bh, a.offset, a.seed_lo, a.seed_hi);
+                        m[2 * half_ + 0] = (r.w[0] >= a.drop_thr ? 0x0000FFFFu : 0u) |
+                                           (r.w[1] >= a.drop_thr ? 0xFFFF0000u : 0u);
+                        m[2 * half_ + 1] = (r.w[2] >= a.drop_thr ? 0x0000FFFFu : 0u) |
+                                           (r.w[3] >= a.drop_thr ? 0xFFFF0000u : 0u);
+                    }
+                    typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+                    u32x4v bits = __builtin_bit_cast(u32x4v, pb[qb][kc]);
+                    bits &= u32x4v{m[0], m[1], m[2], m[3]};
+                    pb[qb][kc] = __builtin_bit_cast(half8, bits);
+                }
+            }
+        }
 
         // ---- O^T += V^T P^T on MFMA ----
         // Source lane l16 of group g points at row 4g + l16/4 (+16 for the second
@@ -474,12 +586,16 @@ void fa2_fwd_kernel(KernelArgs a) {
         // (stage t-1), which the next loads overwrite.
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
-        if (t + 1 < n_tiles) issue_tile(t + 1, Int<1 - ST>{});
+        if (t + 1 < t_end) issue_tile(t + 1, Int<1 - ST>{});
 #pragma unroll
         for (int j = 0; j < SUB; ++j) {
             const int k0 = t * KB + j * BN;
-            if (k0 >= S) break;                         // past the end (last stage only)
-            if (CAUSAL && k0 > qw0 + QW - 1) break;     // above this wave's diagonal
+            if (k0 >= kend) break;                                 // past the keys needed
+            if (MASK == kCausal && k0 > qw0 + QW - 1) break;       // above this wave's diagonal
+            if (MASK == kWindow) {
+                if (k0 > qw0 + QW - 1 + a.wr) break;               // right of this wave's band
+                if (k0 + BN - 1 < qw0 - a.wl) continue;            // left of this wave's band
+            }
             compute_tile(k0, reinterpret_cast<const char*>(smem) + 2 * ((ST * 2 + 0) * LTILE + j * TILE),
                          reinterpret_cast<const char*>(smem) + 2 * ((ST * 2 + 1) * LTILE + j * TILE));
         }
@@ -487,34 +603,36 @@ void fa2_fwd_kernel(KernelArgs a) {
 
     // The ring stage alternates with the tile index; stepping two tiles per
     // iteration makes it a compile-time constant, so LDS offsets are immediates.
-    for (int t = 0; t < n_tiles; t += 2) {
+    for (int t = t_begin; t < t_end; t += 2) {
         tile_step(t, Int<0>{});
-        if (t + 1 < n_tiles) tile_step(t + 1, Int<1>{});
+        if (t + 1 < t_end) tile_step(t + 1, Int<1>{});
     }
 
     // ---- epilogue: O = o / l in fp16, LSE = scale*m + ln(l) ----
-    _Float16* __restrict__ Oh = a.o + head;
+    _Float16* __restrict__ Oh = a.o + b * a.q_sb + h * a.q_sh + (long long)start * q_sr;
+    float* __restrict__ Lh = a.lse + b * a.l_sb + h * a.l_sh + start;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
         float lt = sum_xor16(l_run[qb]);
         lt = sum_xor32(lt);
-        const float inv = 1.0f / lt;
+        const float inv = (DROP ? a.out_scale : 1.0f) / lt;
         const int row = qw0 + 16 * qb + l16;
-        if (row < S) {
+        if (row < len) {
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
                 const f32x4 ov = oacc[db][qb];
-                const half4 h = half4{(_Float16)(ov[0] * inv), (_Float16)(ov[1] * inv),
-                                      (_Float16)(ov[2] * inv), (_Float16)(ov[3] * inv)};
-                *reinterpret_cast<half4*>(Oh + (long long)row * D + 16 * db + 4 * g) = h;
+                const half4 hv = half4{(_Float16)(ov[0] * inv), (_Float16)(ov[1] * inv),
+                                       (_Float16)(ov[2] * inv), (_Float16)(ov[3] * inv)};
+                *reinterpret_cast<half4*>(Oh + (long long)row * q_sr + 16 * db + 4 * g) = hv;
             }
-            if (g == 0) a.lse[(long long)bh * S + row] = (m_run[qb] * a.c + log2f(lt)) * kLn2;
+            if (g == 0) Lh[row] = (m_run[qb] * a.c + log2f(lt)) * kLn2;
         }
     }
 }
 
-// Tile shapes per head dimension: <D, 16-query blocks per wave, waves, keys per tile>.
-// The defaults can be overridden at build time to compare tilings.
+// Tile shapes per head dimension: <D, 16-query blocks per wave, waves, keys per
+// compute tile, compute tiles per ring stage>. The defaults can be overridden at
+// build time to compare tilings.
 #ifndef FA2_D64_QB
 #define FA2_D64_QB 2
 #endif
@@ -542,43 +660,117 @@ void fa2_fwd_kernel(KernelArgs a) {
 using Shape64 = Shape<64, FA2_D64_QB, FA2_D64_NW, FA2_D64_BN, FA2_D64_SUB>;
 using Shape128 = Shape<128, FA2_D128_QB, FA2_D128_NW, FA2_D128_BN, FA2_D128_SUB>;
 
-template <class SH, bool CAUSAL>
-hipError_t launch_shape(const LaunchArgs& a, hipStream_t stream) {
-    KernelArgs k;
+constexpr int kMaxDevices = 64;
+
+template <class SH, int MASK, bool DROP>
+hipError_t launch_shape(const LaunchArgs& a, const KernelArgs& k, hipStream_t stream) {
+    auto kern = fa2_fwd_kernel<SH, MASK, DROP>;
+    if (SH::LDS_BYTES > 65536) {
+        // Opt in to more than 64 KiB of dynamic LDS, once per device.
+        static std::atomic<bool> attr_set[kMaxDevices];
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess) return hipErrorInvalidDevice;
+        if (dev < 0 || dev >= kMaxDevices || !attr_set[dev].load(std::memory_order_acquire)) {
+            hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                               SH::LDS_BYTES);
+            if (e != hipSuccess) return e;
+            if (dev >= 0 && dev < kMaxDevices) attr_set[dev].store(true, std::memory_order_release);
+        }
+    }
+    // One workgroup per (sequence, head, query tile). A 1-D grid keeps
+    // blocks * threads below 2^32; beyond that the id is split over (x, y) with
+    // x a multiple of 8 so that id mod 8 still names the XCD.
+    constexpr unsigned kMaxX = 1u << 22;
+    const unsigned nb = (unsigned)k.nblocks;
+    const dim3 grid(nb <= kMaxX ? nb : kMaxX, nb <= kMaxX ? 1u : (nb + kMaxX - 1) / kMaxX);
+    hipLaunchKernelGGL(kern, grid, dim3(SH::THREADS), SH::LDS_BYTES, stream, k);
+    (void)a;
+    return hipGetLastError();
+}
+
+template <class SH>
+hipError_t launch_d(const LaunchArgs& a, hipStream_t stream) {
+    KernelArgs k{};
     k.q = static_cast<const _Float16*>(a.q);
     k.k = static_cast<const _Float16*>(a.k);
     k.v = static_cast<const _Float16*>(a.v);
     k.o = static_cast<_Float16*>(a.o);
     k.lse = a.lse;
+    k.cu = a.cu_seqlens;
+    const long long D = a.D;
+    if (a.cu_seqlens) {
+        // packed [total, H, D] / [total, H_kv, D]; lse [H, total]
+        k.q_sb = 0;
+        k.q_sh = D;
+        k.q_sr = (int)(a.H * D);
+        k.kv_sb = 0;
+        k.kv_sh = D;
+        k.kv_sr = (int)(a.H_kv * D);
+        k.l_sb = 0;
+        k.l_sh = a.total;
+    } else {
+        // dense [B, H, S, D] / [B, H_kv, S, D]; lse [B, H, S]
+        k.q_sr = (int)D;
+        k.q_sh = (long long)a.S * D;
+        k.q_sb = (long long)a.H * k.q_sh;
+        k.kv_sr = (int)D;
+        k.kv_sh = (long long)a.S * D;
+        k.kv_sb = (long long)a.H_kv * k.kv_sh;
+        k.l_sh = a.S;
+        k.l_sb = (long long)a.H * a.S;
+    }
     k.S = a.S;
+    k.total = a.total;
+    k.H = a.H;
+    k.group = a.H / a.H_kv;
     k.BH = a.B * a.H;
+    k.BHkv = a.B * a.H_kv;
     k.nqt = (a.S + SH::BM - 1) / SH::BM;
     k.nblocks = k.BH * k.nqt;
     k.c = (float)((double)a.scale * kLog2e);
-    auto kern = fa2_fwd_kernel<SH, CAUSAL>;
-    if (SH::LDS_BYTES > 65536) {
-        static bool attr_set = false;  // per process; the attribute is per function
-        if (!attr_set) {
-            hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                               SH::LDS_BYTES);
-            if (e != hipSuccess) return e;
-            attr_set = true;
-        }
+
+    // Window: a negative or out-of-range side is unbounded (S keys).
+    const bool left_open = a.window_left < 0 || a.window_left >= a.S;
+    const bool right_open = a.window_right < 0 || a.window_right >= a.S;
+    int mask = kWindow;
+    if (left_open && right_open) mask = kNoMask;
+    else if (left_open && a.window_right == 0) mask = kCausal;
+    k.wl = left_open ? a.S : a.window_left;
+    k.wr = right_open ? a.S : a.window_right;
+
+    const bool drop = a.dropout_p > 0.0f;
+    k.out_scale = drop ? (float)(1.0 / (1.0 - (double)a.dropout_p)) : 1.0f;
+    k.drop_thr = drop_threshold(a.dropout_p);
+    k.seed_lo = (uint32_t)a.seed;
+    k.seed_hi = (uint32_t)(a.seed >> 32);
+    k.offset = a.offset;
+
+    if (drop) {
+        if (mask == kNoMask) return launch_shape<SH, kNoMask, true>(a, k, stream);
+        if (mask == kCausal) return launch_shape<SH, kCausal, true>(a, k, stream);
+        return launch_shape<SH, kWindow, true>(a, k, stream);
     }
-    hipLaunchKernelGGL(kern, dim3(k.nblocks), dim3(SH::THREADS), SH::LDS_BYTES, stream, k);
-    return hipGetLastError();
+    if (mask == kNoMask) return launch_shape<SH, kNoMask, false>(a, k, stream);
+    if (mask == kCausal) return launch_shape<SH, kCausal, false>(a, k, stream);
+    return launch_shape<SH, kWindow, false>(a, k, stream);
 }
 
 }  // namespace
 
-TileShape tile_shape(int D, int /*causal*/) {
+TileShape tile_shape(int D) {
     if (D == 128) return {Shape128::BM, Shape128::KB, Shape128::THREADS, Shape128::LDS_BYTES};
     return {Shape64::BM, Shape64::KB, Shape64::THREADS, Shape64::LDS_BYTES};
 }
 
+uint32_t drop_threshold(float p) {
+    if (!(p > 0.0f)) return 0u;
+    const double t = std::floor((double)p * 4294967296.0);
+    return t >= 4294967295.0 ? 0xFFFFFFFFu : (uint32_t)t;
+}
+
 hipError_t launch_forward(const LaunchArgs& a, hipStream_t stream) {
-    if (a.D == 64) return a.causal ? launch_shape<Shape64, true>(a, stream) : launch_shape<Shape64, false>(a, stream);
-    return a.causal ? launch_shape<Shape128, true>(a, stream) : launch_shape<Shape128, false>(a, stream);
+    if (a.D == 64) return launch_d<Shape64>(a, stream);
+    return launch_d<Shape128>(a, stream);
 }
 
 }  // namespace fa2

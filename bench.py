@@ -13,6 +13,11 @@ Prints one JSON line:
                workload on this host's cores (a reported baseline, not a target)
 
     python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload 2] [--causal]
+    python bench.py --feature {gqa,mqa,window,varlen,dropout} [--causal]
+
+--feature times one of the production-feature workloads (GQA/MQA, local
+window, packed variable-length sequences, dropout) through fa2_fwd_ex /
+fa2_fwd_varlen instead; their FLOPs are 4*D per admitted (query, key) pair.
 """
 from __future__ import annotations
 
@@ -75,6 +80,93 @@ def cpu_baseline(q, k, v, causal, scale, stride):
                       + ", fp64 oracle, FLOPs counted as 4*D per admitted key"}
 
 
+def admitted_pairs(L: int, wl: int, wr: int, causal: bool) -> int:
+    """Number of admissible (query, key) pairs of one head of a length-L sequence."""
+    import numpy as np
+    if causal:
+        wr = 0
+    i = np.arange(L, dtype=np.int64)
+    lo = np.maximum(0, i - wl) if wl >= 0 else np.zeros_like(i)
+    hi = np.minimum(L - 1, i + wr) if wr >= 0 else np.full_like(i, L - 1)
+    return int(np.sum(hi - lo + 1))
+
+
+def feature_setup(key: str, causal: bool, dev):
+    """Inputs, the launch closure, FLOPs and a CPU-baseline closure of a
+    production-feature workload."""
+    import numpy as np
+    import torch
+    import attention_forward_fa2_amd as fa2
+    from fa2_inputs import FEATURES, make_feature_inputs
+    f = FEATURES[key]
+    wl, wr = f.window
+    if causal:
+        wr = 0
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    if f.packed:
+        q, k, v, cu = make_feature_inputs(key)
+        total = int(cu[-1])
+        qt, kt, vt = (torch.from_numpy(x).to(dev) for x in (q, k, v))
+        cut = torch.from_numpy(cu).to(dev)
+        o = torch.empty_like(qt)
+        lse = torch.empty((f.H, total), dtype=torch.float32, device=dev)
+        max_len = int(np.max(np.diff(cu)))
+
+        def step():
+            st = fa2.fa2_fwd_varlen(qt.data_ptr(), kt.data_ptr(), vt.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                    cut.data_ptr(), len(cu) - 1, total, max_len, f.H, f.H_kv, f.D, wl, wr,
+                                    f.dropout_p, f.seed, 0, f.scale, stream)
+            if st != 0:
+                raise fa2.FA2Error(st)
+        pairs = f.H * sum(admitted_pairs(int(L), wl, wr, causal) for L in np.diff(cu))
+        cfg = {"sequences": len(cu) - 1, "total_rows": total, "max_seqlen": max_len, "H": f.H, "H_kv": f.H_kv,
+               "D": f.D}
+
+        def cpu():
+            import oracle
+            s = int(np.argmax(np.diff(cu)))
+            a, e = int(cu[s]), int(cu[s + 1])
+            lib = oracle.load()
+            qa, ka, va = (np.ascontiguousarray(x[a:e]).astype(np.float64) for x in (q, k, v))
+            t0 = time.perf_counter()
+            oracle.attention_varlen(qa, ka, va, np.array([0, e - a]), float(np.float32(f.scale)), window=(wl, wr),
+                                    dropout_p=f.dropout_p, seed=f.seed, lib=lib)
+            secs = time.perf_counter() - t0
+            fl = 4.0 * f.D * f.H * admitted_pairs(e - a, wl, wr, causal)
+            return fl, secs, f"the longest sequence ({e - a} rows, all {f.H} heads)"
+    else:
+        q, k, v = make_feature_inputs(key)
+        qt, kt, vt = (torch.from_numpy(x).to(dev) for x in (q, k, v))
+        o = torch.empty_like(qt)
+        lse = torch.empty((f.B, f.H, f.S), dtype=torch.float32, device=dev)
+
+        def step():
+            st = fa2.fa2_fwd_ex(qt.data_ptr(), kt.data_ptr(), vt.data_ptr(), o.data_ptr(), lse.data_ptr(), f.B,
+                                f.H, f.H_kv, f.S, f.D, wl, wr, f.dropout_p, f.seed, 0, f.scale, stream)
+            if st != 0:
+                raise fa2.FA2Error(st)
+        pairs = f.B * f.H * admitted_pairs(f.S, wl, wr, causal)
+        cfg = {"B": f.B, "H": f.H, "H_kv": f.H_kv, "S": f.S, "D": f.D}
+
+        def cpu():
+            import oracle
+            stride = 8
+            rows = np.arange(0, f.B * f.H * f.S, stride, dtype=np.int64)
+            qa, ka, va = (x.astype(np.float64) for x in (q, k, v))
+            t0 = time.perf_counter()
+            oracle.attention_ex(qa, ka, va, float(np.float32(f.scale)), window=(wl, wr), dropout_p=f.dropout_p,
+                                seed=f.seed, rows=rows)
+            secs = time.perf_counter() - t0
+            i = rows % f.S
+            lo = np.maximum(0, i - wl) if wl >= 0 else 0
+            hi = np.minimum(f.S - 1, i + wr) if wr >= 0 else f.S - 1
+            fl = float(np.sum(4.0 * f.D * (hi - lo + 1)))
+            return fl, secs, f"every {stride}th query row ({len(rows)} of {f.B * f.H * f.S} rows)"
+    cfg.update({"window": [wl, wr], "dropout_p": f.dropout_p, "causal": causal, "scale": f.scale,
+                "inputs": f"fp16 iid normal, seeds {f.seed}+{{0,1,2}}"})
+    return f, step, 4.0 * f.D * pairs, cfg, cpu
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -82,6 +174,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--causal", action="store_true", help="run the causal variant of the workload")
+    ap.add_argument("--feature", choices=["gqa", "mqa", "window", "varlen", "dropout"], default=None,
+                    help="time a production-feature workload instead of a plain one")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-stride", type=int, default=1, help="oracle sample: every n-th row (1 = all rows)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -111,24 +205,34 @@ def main():
     import attention_forward_fa2_amd as fa2
     from fa2_inputs import WORKLOADS, make_inputs
 
-    w = WORKLOADS[args.workload]
-    causal = bool(args.causal) or w.causal_modes == (True,)
-    if causal not in w.causal_modes:
-        raise SystemExit(f"workload {args.workload} is not run in this mode")
     dev = torch.device("cuda:0")
-    log(f"bench: workload {args.workload} ({w.name}) causal={causal} steps={args.steps} warmup={args.warmup}")
-    q, k, v = make_inputs(args.workload)
-    qt, kt, vt = (torch.from_numpy(x).to(dev) for x in (q, k, v))
-    o = torch.empty_like(qt)
-    lse = torch.empty((w.B, w.H, w.S), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
-    sp = stream.cuda_stream
-    ptrs = (qt.data_ptr(), kt.data_ptr(), vt.data_ptr(), o.data_ptr(), lse.data_ptr())
+    if args.feature:
+        f, step, flops, cfg, cpu_fn = feature_setup(args.feature, bool(args.causal), dev)
+        causal = bool(args.causal)
+        log(f"bench: feature workload {args.feature} ({f.name}) causal={causal} steps={args.steps}")
+        workload_name = f"attention fwd {f.name}{' causal' if causal else ''}"
+    else:
+        w = WORKLOADS[args.workload]
+        causal = bool(args.causal) or w.causal_modes == (True,)
+        if causal not in w.causal_modes:
+            raise SystemExit(f"workload {args.workload} is not run in this mode")
+        log(f"bench: workload {args.workload} ({w.name}) causal={causal} steps={args.steps} warmup={args.warmup}")
+        q, k, v = make_inputs(args.workload)
+        qt, kt, vt = (torch.from_numpy(x).to(dev) for x in (q, k, v))
+        o = torch.empty_like(qt)
+        lse = torch.empty((w.B, w.H, w.S), dtype=torch.float32, device=dev)
+        sp = stream.cuda_stream
+        ptrs = (qt.data_ptr(), kt.data_ptr(), vt.data_ptr(), o.data_ptr(), lse.data_ptr())
 
-    def step():
-        st = fa2.fa2_fwd(*ptrs, w.B, w.H, w.S, w.D, int(causal), w.scale, sp)
-        if st != 0:
-            raise fa2.FA2Error(st)
+        def step():
+            st = fa2.fa2_fwd(*ptrs, w.B, w.H, w.S, w.D, int(causal), w.scale, sp)
+            if st != 0:
+                raise fa2.FA2Error(st)
+        flops = w.flops(causal)
+        workload_name = f"attention fwd {w.name} {'causal' if causal else 'non-causal'}"
+        cfg = {"B": w.B, "H": w.H, "S": w.S, "D": w.D, "causal": causal, "scale": w.scale,
+               "inputs": "fp16 iid normal, seeds 1000*w+{0,1,2}"}
 
     for _ in range(args.warmup):
         step()
@@ -156,10 +260,9 @@ def main():
     log(f"bench: {ms_per_step * 1e3:.1f} us/step, kernel avg {kern_avg_ms * 1e3:.1f} us "
         f"(min {kern_ms[0] * 1e3:.1f}, median {kern_ms[len(kern_ms) // 2] * 1e3:.1f})")
 
-    flops = w.flops(causal)
     value = flops / (ms_per_step * 1e-3) / 1e12
     achieved = flops / (kern_avg_ms * 1e-3) / 1e12
-    traffic = measured_traffic(args.workload, causal)
+    traffic = None if args.feature else measured_traffic(args.workload, causal)
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_F16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4),
                 "traffic": traffic}
@@ -167,11 +270,20 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         log("bench: timing the CPU oracle on a sample")
-        cpu = cpu_baseline(q, k, v, causal, float(np.float32(w.scale)), args.cpu_stride)
+        if args.feature:
+            import oracle
+            fl, secs, sample = cpu_fn()
+            cpu = {"value": fl / secs / 1e12, "unit": "TFLOP/s", "cores": oracle.max_threads(), "kind": "oracle",
+                   "seconds": secs, "sample": sample + " of the workload, fp64 oracle, FLOPs counted as 4*D per "
+                                                       "admitted key"}
+        else:
+            cpu = cpu_baseline(q, k, v, causal, float(np.float32(w.scale)), args.cpu_stride)
         log(f"bench: oracle {cpu['seconds']:.1f} s on {cpu['cores']} threads")
 
     rec = {
-        "metric": "FA2 fwd TFLOP/s (4*B*H*S^2*D, 1/2 causal) and % of MI355X FP16 MFMA peak",
+        "metric": ("FA2 fwd TFLOP/s (4*D per admitted query-key pair) and % of MI355X FP16 MFMA peak"
+                   if args.feature else
+                   "FA2 fwd TFLOP/s (4*B*H*S^2*D, 1/2 causal) and % of MI355X FP16 MFMA peak"),
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -183,9 +295,7 @@ def main():
         "vs_baseline": None,
         "dtype": "f16",
         "data": "synthetic",
-        "config": {"workload": f"attention fwd {w.name} {'causal' if causal else 'non-causal'}",
-                   "B": w.B, "H": w.H, "S": w.S, "D": w.D, "causal": causal, "scale": w.scale,
-                   "inputs": "fp16 iid normal, seeds 1000*w+{0,1,2}",
+        "config": {"workload": workload_name, **cfg,
                    "pct_of_fp16_mfma_peak": round(100 * value / MFMA_F16_PEAK_TFLOPS, 2)},
         "roofline": roofline,
         "cpu_baseline": cpu,

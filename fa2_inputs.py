@@ -93,3 +93,67 @@ def sample_rows(cid: int, n: int, seed: int = 7) -> np.ndarray:
             fixed.append(hd * w.S + i)
     picks = g.integers(0, heads * w.S, size=n)
     return np.unique(np.concatenate([np.array(fixed, dtype=np.int64), picks.astype(np.int64)]))
+
+
+# ---- workloads of the production features (GQA/MQA, local window, packed
+# variable-length sequences, dropout). The page lists these features without
+# measuring them; the shapes below keep the head dimension and value
+# distribution of the workloads above.
+
+@dataclass(frozen=True)
+class FeatureWorkload:
+    key: str
+    name: str
+    B: int                  # batch, or number of packed sequences
+    H: int
+    H_kv: int
+    S: int                  # sequence length, or the longest packed sequence
+    D: int
+    window: tuple           # (left, right); -1 = unbounded side
+    dropout_p: float
+    seed: int
+    lens: tuple = ()        # packed sequence lengths (varlen only)
+
+    @property
+    def scale(self) -> float:
+        return float(np.float32(1.0 / np.sqrt(float(self.D))))
+
+    @property
+    def packed(self) -> bool:
+        return bool(self.lens)
+
+
+def _packed_lengths(seed: int, n: int, lo: int, hi: int) -> tuple:
+    g = np.random.Generator(np.random.PCG64(seed))
+    return tuple(int(x) for x in g.integers(lo, hi + 1, size=n))
+
+
+FEATURES = {
+    "gqa": FeatureWorkload("gqa", "GQA B4 H8 H_kv2 S4096 D64", 4, 8, 2, 4096, 64, (-1, -1), 0.0, 6000),
+    "mqa": FeatureWorkload("mqa", "MQA B4 H8 H_kv1 S4096 D64", 4, 8, 1, 4096, 64, (-1, -1), 0.0, 6100),
+    "window": FeatureWorkload("window", "local window (1024, 1024) B4 H8 S8192 D64", 4, 8, 8, 8192, 64,
+                              (1024, 1024), 0.0, 6200),
+    "varlen": FeatureWorkload("varlen", "packed 24 sequences of 64..4096 rows, H8 D64", 24, 8, 8, 4096, 64,
+                              (-1, -1), 0.0, 6300, _packed_lengths(6399, 24, 64, 4096)),
+    "dropout": FeatureWorkload("dropout", "dropout p=0.1 B4 H8 S4096 D64", 4, 8, 8, 4096, 64, (-1, -1),
+                               float(np.float32(0.1)), 6400),
+}
+
+
+def make_packed(seed: int, lens, H: int, H_kv: int, D: int, sigma_qk: float = 1.0, sigma_v: float = 1.0):
+    """(q [total,H,D], k [total,H_kv,D], v [total,H_kv,D], cu_seqlens int32
+    [n+1]) for packed sequences of the given lengths; seeds seed+0/1/2."""
+    cu = np.concatenate([[0], np.cumsum(np.asarray(lens, dtype=np.int64))]).astype(np.int32)
+    total = int(cu[-1])
+    return (normal_f16(seed, (total, H, D), sigma_qk), normal_f16(seed + 1, (total, H_kv, D), sigma_qk),
+            normal_f16(seed + 2, (total, H_kv, D), sigma_v), cu)
+
+
+def make_feature_inputs(key: str):
+    """Inputs of feature workload ``key``: (q, k, v) dense [B,H,S,D] /
+    [B,H_kv,S,D], or (q, k, v, cu_seqlens) packed."""
+    f = FEATURES[key]
+    if f.packed:
+        return make_packed(f.seed, f.lens, f.H, f.H_kv, f.D)
+    return (normal_f16(f.seed, (f.B, f.H, f.S, f.D)), normal_f16(f.seed + 1, (f.B, f.H_kv, f.S, f.D)),
+            normal_f16(f.seed + 2, (f.B, f.H_kv, f.S, f.D)))

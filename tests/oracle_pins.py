@@ -207,3 +207,171 @@ def pin_dominant_key(lib):
 ALL_PINS = [pin_dominant_key, pin_worked_2x2, pin_worked_4x4, pin_uniform_scores, pin_causal_first_row,
             pin_convexity, pin_probabilities, pin_key_shift, pin_permutations,
             pin_library_softmax, pin_rectangular_head_dim]
+
+
+# ---- the production features of §"哪些结论可以迁移，哪些只是本例特例" ----
+# GQA/MQA, local window, packed variable-length sequences and dropout, under the
+# readings stated at the top of oracle/attn_oracle.c.
+
+def pin_philox_known_answers(lib):
+    """Philox4x32-10 reproduces the known-answer vectors its authors publish."""
+    g = json.load(open(os.path.join(GOLDEN, "philox4x32_10_kat.json")))
+    for vec in g["vectors"]:
+        got = oracle.philox4x32_10([int(x, 16) for x in vec["counter"]], [int(x, 16) for x in vec["key"]], lib=lib)
+        assert got == [int(x, 16) for x in vec["out"]], f"Philox KAT {vec['counter']}: got {[hex(x) for x in got]}"
+
+
+def _band_mask(S, wl, wr):
+    i = np.arange(S)[:, None]
+    j = np.arange(S)[None, :]
+    ok = np.ones((S, S), dtype=bool)
+    if wl >= 0:
+        ok &= j >= i - wl
+    if wr >= 0:
+        ok &= j <= i + wr
+    return ok
+
+
+WINDOWS = [(-1, -1), (-1, 0), (0, 0), (3, 2), (0, 5), (7, -1), (-1, 4), (1, 0), (40, 40)]
+
+
+def pin_window_uniform(lib):
+    """Q = 0: O_i is the mean of v_j over the window and LSE_i = ln(window
+    size), which fixes both window bounds to the key."""
+    B, H, S, D = 1, 2, 29, 4
+    q = np.zeros((B, H, S, D))
+    k, v = _rand(81, (B, H, S, D)), _rand(82, (B, H, S, D))
+    for wl, wr in WINDOWS:
+        ok = _band_mask(S, wl, wr).astype(np.float64)
+        cnt = ok.sum(axis=1)
+        O, L = oracle.attention_ex(q, k, v, 0.125, window=(wl, wr), lib=lib)
+        _close(O, (ok @ v) / cnt[:, None], 1e-13, f"window {wl},{wr} Q=0 O")
+        _close(L, np.broadcast_to(np.log(cnt), (B, H, S)), 1e-13, f"window {wl},{wr} Q=0 LSE")
+
+
+def pin_window_library_softmax(lib):
+    """Against scipy's softmax / logsumexp of the full score matrix with -inf
+    outside the band, for GQA heads (query head h reads K/V head h // group)."""
+    B, H, H_kv, S, D = 2, 6, 2, 23, 8
+    q, k, v = _rand(91, (B, H, S, D), 2.0), _rand(92, (B, H_kv, S, D), 2.0), _rand(93, (B, H_kv, S, D))
+    kr = np.repeat(k, H // H_kv, axis=1)
+    vr = np.repeat(v, H // H_kv, axis=1)
+    scale = 0.3
+    for wl, wr in WINDOWS:
+        s = scale * (q @ np.swapaxes(kr, -1, -2))
+        s = np.where(_band_mask(S, wl, wr), s, -np.inf)
+        O, L = oracle.attention_ex(q, k, v, scale, window=(wl, wr), lib=lib)
+        _close(O, softmax(s, axis=-1) @ vr, 1e-12, f"window {wl},{wr} scipy O")
+        _close(L, logsumexp(s, axis=-1), 1e-12, f"window {wl},{wr} scipy LSE")
+
+
+def pin_window_zero(lib):
+    """Window (0, 0): each query sees only its own key, so O_i = v_i and
+    LSE_i = scale * q_i . k_i."""
+    B, H, S, D = 1, 3, 11, 8
+    q, k, v = _rand(95, (B, H, S, D)), _rand(96, (B, H, S, D)), _rand(97, (B, H, S, D))
+    O, L = oracle.attention_ex(q, k, v, 0.5, window=(0, 0), lib=lib)
+    _close(O, v, 0.0, "window 0,0 O")
+    _close(L, 0.5 * np.einsum("bhsd,bhsd->bhs", q, k), 1e-13, "window 0,0 LSE")
+
+
+def pin_varlen_is_per_sequence(lib):
+    """Packed sequences give, row for row, the dense result of each sequence on
+    its own (empty sequences included), with GQA heads and a window."""
+    H, H_kv, D = 4, 2, 8
+    lens = [5, 0, 17, 1, 9]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    total = int(cu[-1])
+    q, k, v = _rand(101, (total, H, D)), _rand(102, (total, H_kv, D)), _rand(103, (total, H_kv, D))
+    for window in ((-1, -1), (-1, 0), (2, 1)):
+        O, L = oracle.attention_varlen(q, k, v, cu, 0.25, window=window, lib=lib)
+        for s, (a, e) in enumerate(zip(cu, cu[1:])):
+            if e == a:
+                continue
+            qs = np.ascontiguousarray(q[a:e].transpose(1, 0, 2))[None]
+            ks = np.ascontiguousarray(np.repeat(k[a:e], H // H_kv, axis=1).transpose(1, 0, 2))[None]
+            vs = np.ascontiguousarray(np.repeat(v[a:e], H // H_kv, axis=1).transpose(1, 0, 2))[None]
+            s_ = 0.25 * (qs @ np.swapaxes(ks, -1, -2))
+            s_ = np.where(_band_mask(e - a, *window), s_, -np.inf)
+            _close(O[a:e], (softmax(s_, axis=-1) @ vs)[0].transpose(1, 0, 2), 1e-12, f"varlen seq {s} O {window}")
+            _close(L[:, a:e], logsumexp(s_, axis=-1)[0], 1e-12, f"varlen seq {s} LSE {window}")
+
+
+def _keep_mask(S, bh, seed, offset, thr, lib):
+    """z_ij from the generator: word j%4 of Philox(j//4, i, bh, offset) >= thr."""
+    z = np.zeros((S, S))
+    for i in range(S):
+        for j4 in range((S + 3) // 4):
+            r = oracle.philox4x32_10([j4, i, bh, offset], [seed & 0xFFFFFFFF, seed >> 32], lib=lib)
+            for e in range(4):
+                if 4 * j4 + e < S:
+                    z[i, 4 * j4 + e] = 1.0 if r[e] >= thr else 0.0
+    return z
+
+
+def pin_dropout_mask(lib):
+    """Q = 0 and V = I (D = S): O_ij = P_ij z_ij / (1 - p) with P_ij = 1/n_i,
+    so O exposes every keep decision z_ij, which must be the generator's, with
+    the counter (j // 4, i, b*H + h, offset) and the key from the seed. LSE is
+    that of the softmax before dropout."""
+    B, H, S = 1, 2, 10
+    q = np.zeros((B, H, S, S))
+    k = _rand(111, (B, H, S, S))
+    v = np.broadcast_to(np.eye(S), (B, H, S, S)).copy()
+    p = float(np.float32(0.3))
+    seed, offset = 0x1234_5678_9ABC_DEF0, 77
+    thr = oracle.dropout_threshold(p)
+    for wl, wr in ((-1, -1), (-1, 0)):
+        ok = _band_mask(S, wl, wr).astype(np.float64)
+        n = ok.sum(axis=1)
+        O, L = oracle.attention_ex(q, k, v, 0.125, window=(wl, wr), dropout_p=p, seed=seed, offset=offset, lib=lib)
+        for h in range(H):
+            z = _keep_mask(S, h, seed, offset, thr, lib)
+            _close(O[0, h], ok * z / (n[:, None] * (1.0 - p)), 1e-14, f"dropout mask head {h} window {wl},{wr}")
+        _close(L, np.broadcast_to(np.log(n), (B, H, S)), 1e-13, f"dropout LSE unchanged window {wl},{wr}")
+
+
+def pin_dropout_statistics(lib):
+    """Over many offsets the keep rate is 1 - p (binomial, 6 sigma) and the
+    dropped output is an unbiased estimate of the plain one (mean within 6
+    standard errors of its own spread)."""
+    B, H, S, D = 1, 1, 24, 4
+    q, k, v = _rand(121, (B, H, S, D)), _rand(122, (B, H, S, D)), _rand(123, (B, H, S, D))
+    p = float(np.float32(0.25))
+    O0, L0 = oracle.attention_ex(q, k, v, 0.5, lib=lib)
+    draws = []
+    for off in range(300):
+        O, L = oracle.attention_ex(q, k, v, 0.5, dropout_p=p, seed=99, offset=off, lib=lib)
+        _close(L, L0, 0.0, "dropout leaves LSE unchanged")
+        draws.append(O)
+    draws = np.array(draws)
+    mean, se = draws.mean(axis=0), draws.std(axis=0) / math.sqrt(len(draws))
+    z = np.abs(mean - O0) / np.maximum(se, 1e-12)
+    assert np.max(z) < 6.0, f"dropout output biased: max z-score {np.max(z):.2f}"
+    n = 0
+    kept = 0
+    thr = oracle.dropout_threshold(p)
+    for off in range(40):
+        for i in range(8):
+            for j4 in range(6):
+                r = oracle.philox4x32_10([j4, i, 0, off], [99, 0], lib=lib)
+                kept += sum(1 for w in r if w >= thr)
+                n += 4
+    sigma = math.sqrt(n * p * (1 - p))
+    assert abs(kept - n * (1 - p)) < 6 * sigma, f"keep rate {kept / n:.4f} vs {1 - p}"
+
+
+def pin_dropout_off(lib):
+    """p = 0 is the plain definition, whatever the seed."""
+    B, H, S, D = 1, 2, 13, 8
+    q, k, v = _rand(131, (B, H, S, D)), _rand(132, (B, H, S, D)), _rand(133, (B, H, S, D))
+    for causal in (False, True):
+        O0, L0 = oracle.attention(q, k, v, causal, 0.2, lib=lib)
+        O1, L1 = oracle.attention_ex(q, k, v, 0.2, window=(-1, 0 if causal else -1), dropout_p=0.0, seed=5,
+                                     offset=3, lib=lib)
+        _close(O1, O0, 0.0, "p=0 O")
+        _close(L1, L0, 0.0, "p=0 LSE")
+
+
+ALL_PINS += [pin_philox_known_answers, pin_window_uniform, pin_window_library_softmax, pin_window_zero,
+             pin_varlen_is_per_sequence, pin_dropout_mask, pin_dropout_statistics, pin_dropout_off]

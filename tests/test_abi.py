@@ -99,10 +99,12 @@ def test_lse_needs_only_4_byte_alignment():
 
 
 def test_overflow():
-    assert call(S=1 << 25, D=64) == 5          # S*D = 2^31
-    assert call(S=1 << 24, D=128) == 5         # S*D = 2^31
-    assert call(S=(1 << 24) - 1, D=128, o=Q) == 6
-    assert call(S=(1 << 25) - 1, D=64, o=Q) == 6
+    assert call(S=1 << 29, D=64) == 5          # row index plus a window side must stay below 2^31
+    assert call(S=(1 << 29) - 1, D=128, o=Q) == 6
+    # tensors far beyond 2^31 elements are fine (64-bit addressing) ...
+    assert call(B=64, H=64, S=1 << 20, D=128, o=Q) == 6
+    # ... but the grid must fit in 2^31 - 1 workgroups
+    assert call(B=1 << 16, H=1 << 12, S=1 << 12, D=64) == 5
 
 
 def test_valid_arguments_reach_the_alias_check():
@@ -123,7 +125,82 @@ def test_error_order():
     assert call(q=None, B=0, scale=-1.0) == 1
     assert call(B=0, scale=-1.0, q=Q + 2) == 2
     assert call(scale=-1.0, q=Q + 2) == 3
-    assert call(q=Q + 2, S=1 << 25) == 4
+    assert call(q=Q + 2, S=1 << 29) == 4
+
+
+def call_ex(q=Q, k=K, v=V, o=O, lse=L, B=1, H=4, H_kv=2, S=128, D=64, wl=-1, wr=-1, p=0.0, seed=0, offset=0,
+            scale=0.125):
+    return fa2.fa2_fwd_ex(q, k, v, o, lse, B, H, H_kv, S, D, wl, wr, p, seed, offset, scale, None)
+
+
+CU = BASE + 5 * GAP
+
+
+def call_varlen(q=Q, k=K, v=V, o=O, lse=L, cu=CU, nseq=3, total=300, max_seqlen=200, H=4, H_kv=1, D=128,
+                wl=-1, wr=-1, p=0.0, seed=0, offset=0, scale=0.125):
+    return fa2.fa2_fwd_varlen(q, k, v, o, lse, cu, nseq, total, max_seqlen, H, H_kv, D, wl, wr, p, seed, offset,
+                              scale, None)
+
+
+@pytest.mark.parametrize("which", range(5))
+def test_ex_null_pointer(which):
+    ptrs = [Q, K, V, O, L]
+    ptrs[which] = None
+    assert call_ex(*ptrs) == 1
+
+
+@pytest.mark.parametrize("which", range(6))
+def test_varlen_null_pointer(which):
+    ptrs = [Q, K, V, O, L, CU]
+    ptrs[which] = None
+    assert call_varlen(*ptrs) == 1
+
+
+@pytest.mark.parametrize("kw", [dict(H_kv=0), dict(H_kv=3), dict(H=2, H_kv=4), dict(B=0), dict(S=0), dict(D=96)])
+def test_ex_bad_shape(kw):
+    assert call_ex(**kw) == 2
+
+
+@pytest.mark.parametrize("kw", [dict(nseq=0), dict(total=0), dict(max_seqlen=0), dict(H_kv=3), dict(D=32),
+                                dict(H=0)])
+def test_varlen_bad_shape(kw):
+    assert call_varlen(**kw) == 2
+
+
+@pytest.mark.parametrize("kw", [dict(wl=-2), dict(wr=-5), dict(p=-0.1), dict(p=1.0), dict(p=1.5),
+                                dict(p=float("nan")), dict(p=float("inf"))])
+def test_bad_window_or_dropout(kw):
+    assert call_ex(**kw) == 9
+    assert call_varlen(**kw) == 9
+
+
+def test_ex_and_varlen_accept_valid_extras():
+    # every call here also aliases o with q, the last check
+    for kw in (dict(wl=0, wr=0), dict(wl=5, wr=-1), dict(wl=-1, wr=0), dict(p=0.0), dict(p=0.999, seed=2**64 - 1),
+               dict(H=8, H_kv=1), dict(H=8, H_kv=8), dict(offset=2**32 - 1)):
+        assert call_ex(o=Q, **kw) == 6
+        assert call_varlen(o=Q, **kw) == 6
+
+
+def test_varlen_alignment_and_alias():
+    assert call_varlen(cu=CU + 2) == 4
+    assert call_varlen(cu=CU + 4, o=Q) == 6     # 4-byte alignment is enough
+    assert call_varlen(cu=O + 64) == 6          # the table inside o
+    assert call_varlen(lse=CU) == 6
+
+
+def test_varlen_overflow():
+    assert call_varlen(max_seqlen=1 << 29) == 5
+    assert call_varlen(H=1 << 19, H_kv=1 << 19, D=64) == 5   # a K/V row stride too large for 32-bit lane offsets
+    assert call_varlen(H=1 << 10, H_kv=1 << 10, D=128, o=Q) == 6
+
+
+def test_extended_error_order():
+    # scale beats window/dropout beats alignment
+    assert call_ex(scale=0.0, p=2.0, q=Q + 2) == 3
+    assert call_ex(p=2.0, q=Q + 2) == 9
+    assert call_varlen(wl=-3, cu=CU + 1) == 9
+    assert call_ex(H_kv=3, p=2.0) == 2
 
 
 def test_kernel_config():
@@ -147,6 +224,16 @@ def test_forward_rejects_bad_tensors():
         fa2.forward(q, q[:, :, :4], q)
     with pytest.raises(ValueError):
         fa2.forward(q, q, q)  # CPU tensors: there is no CPU path
+    with pytest.raises(ValueError):
+        fa2.forward_ex(q, q, q, window=(2, 2))
+    with pytest.raises(ValueError):
+        fa2.forward_ex(q, q[:, :, :4], q[:, :, :4])
+    p = torch.zeros((8, 1, 64), dtype=torch.float16)
+    cu = torch.tensor([0, 8], dtype=torch.int32)
+    with pytest.raises(ValueError):
+        fa2.forward_varlen(p, p, p, cu)
+    with pytest.raises(ValueError):
+        fa2.forward_varlen(p, p, p, cu.long())
 
 
 def test_no_fallback_when_library_missing(tmp_path):

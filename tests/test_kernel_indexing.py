@@ -3,9 +3,16 @@
 Restates, in numpy, the address formulas of
 attention_forward_fa2_amd/csrc/fa2_fwd_kernel.hip for the tile shapes the
 library uses and checks, for many tensor shapes, that
-  * the workgroup -> (head, query tile) mapping is a bijection,
+  * the workgroup -> (head, query tile) mapping is a bijection, also when
+    query heads share K/V heads (GQA/MQA),
   * every global load (Q rows, K/V tiles, clamped ragged tiles) and every store
-    (O, LSE) stays inside its tensor,
+    (O, LSE) stays inside its tensor and inside its own sequence, for the
+    dense [B,H,S,D] layout and for packed sequences [total,H,D] (including
+    malformed sequence tables, which the kernel clamps),
+  * the K/V stages a workgroup scans and the compute tiles each wave keeps
+    cover every admissible key of its rows (causal and local windows), and a
+    tile the kernel does not mask holds only admissible keys,
+  * the dropout counter of each probability register names that register's key,
   * every LDS destination and LDS read stays inside the ring,
   * the hoisted per-lane LDS read offsets equal the per-row formulas,
   * the XOR swizzles put each ds_read_b128 quarter-wave (K) and each
@@ -31,13 +38,15 @@ SHAPES = {64: (2, 8, 64, 2), 128: (2, 8, 64, 2)}
 VARIANTS = [(2, 8, 64, 1), (2, 8, 64, 2), (2, 4, 64, 1), (2, 4, 64, 2), (4, 4, 64, 1)]
 
 
-def block_map(BH, nqt, causal):
+def block_map(BH, nqt, causal, group=1):
     nb = BH * nqt
     bid = np.arange(nb)
     xcd, slot = bid & 7, bid >> 3
-    if causal and BH % 8 == 0:
-        hx = BH >> 3
-        return xcd + 8 * (slot % hx), nqt - 1 - slot // hx
+    BHkv = BH // group
+    if causal and BHkv % 8 == 0:
+        per_tile = (BHkv >> 3) * group
+        r = slot % per_tile
+        return (xcd + 8 * (r // group)) * group + r % group, nqt - 1 - slot // per_tile
     per, rem = nb >> 3, nb & 7
     logical = xcd * per + np.minimum(xcd, rem) + slot
     if causal:
@@ -54,60 +63,148 @@ def test_block_mapping_is_a_bijection(BH, nqt, causal):
     assert len(set(zip(bh.tolist(), qt.tolist()))) == BH * nqt
 
 
-def emulate(B, H, S, D, causal, shape=None):
+@pytest.mark.parametrize("BHkv,group", [(8, 2), (8, 4), (16, 3), (24, 8), (32, 1), (4, 4), (12, 2), (1, 32)])
+@pytest.mark.parametrize("nqt", [1, 5, 16])
+def test_gqa_causal_mapping(BHkv, group, nqt):
+    """Causal with GQA: a bijection, and when the K/V heads split evenly over
+    the 8 XCDs every query head of one K/V head lands on one XCD."""
+    BH = BHkv * group
+    bh, qt = block_map(BH, nqt, True, group)
+    assert bh.min() >= 0 and bh.max() < BH and qt.min() >= 0 and qt.max() < nqt
+    assert len(set(zip(bh.tolist(), qt.tolist()))) == BH * nqt
+    if BHkv % 8 == 0:
+        xcd = np.arange(BH * nqt) & 7
+        kv = bh // group
+        for h in range(BHkv):
+            assert len(set(xcd[kv == h].tolist())) == 1
+
+
+def emulate(B, H, S, D, causal, shape=None, H_kv=None, cu=None, total=None, window=None):
+    """Walk every workgroup and wave of one launch with the kernel's formulas.
+    Dense: q/o [B,H,S,D], k/v [B,H_kv,S,D], lse [B,H,S]. Packed (cu given): B
+    sequences, q/o [total,H,D], k/v [total,H_kv,D], lse [H,total], S = longest
+    sequence. window = (wl, wr) as the host passes it (after clamping unbounded
+    sides to S); causal = (S, 0) uses the causal kernel."""
     QB, NW, BN, SUB = shape or SHAPES[D]
+    H_kv = H_kv or H
+    group = H // H_kv
     QW, BM = 16 * QB, 16 * QB * NW
-    CPR, TILE, DB, NKC, NKB, DK = D // 8, BN * D, D // 16, BN // 32, BN // 16, D // 32
+    CPR, DB, DK = D // 8, D // 16, D // 32
     KB, LTILE = SUB * BN, SUB * BN * D
     LOADS = LTILE // 8 // 64 // NW
     RPL = NW * 64 // CPR
     assert RPL % 16 == 0
+    mode = "window" if window is not None else ("causal" if causal else "none")
+    wl, wr = window if window is not None else (S, 0 if causal else S)
+    if cu is None:
+        q_sr, q_sh, q_sb = D, S * D, H * S * D
+        kv_sr, kv_sh, kv_sb = D, S * D, H_kv * S * D
+        l_sh, l_sb = S, H * S
+        n_q, n_kv, n_l = B * H * S * D, B * H_kv * S * D, B * H * S
+        rows_total = None
+    else:
+        q_sr, q_sh, q_sb = H * D, D, 0
+        kv_sr, kv_sh, kv_sb = H_kv * D, D, 0
+        l_sh, l_sb = total, 0
+        n_q, n_kv, n_l = total * H * D, total * H_kv * D, H * total
     lane = np.arange(64)
     l16, g = lane & 15, lane >> 4
     nqt = -(-S // BM)
-    bh, qt = block_map(B * H, nqt, causal)
-    total = B * H * S * D
-    for wave in range(NW):
-        qw0 = qt * BM + wave * QW
-        # Q loads (rows clamped to S-1)
-        for qb in range(QB):
-            row = np.minimum(qw0[:, None] + 16 * qb + l16[None, :], S - 1)
-            for kk in range(DK):
-                off = bh[:, None] * S * D + row * D + 32 * kk + 8 * g[None, :]
-                assert off.min() >= 0 and (off + 8).max() <= total
-        # K/V direct-to-LDS loads: the kernel keeps one lane offset (row0, pc0)
-        # per tensor and steps the scalar base by RPL rows per load
-        row0, pc0 = (wave * 64 + lane) // CPR, lane % CPR
-        for i in range(LOADS):
-            c = (i * NW + wave) * 64 + lane
-            r, pc = c // CPR, c % CPR
-            assert np.array_equal(r, row0 + i * RPL) and np.array_equal(pc, pc0)
-            dst = 2 * (i * NW + wave) * 512 + 16 * lane
-            assert dst.min() >= 0 and (dst + 16).max() <= 2 * LTILE
-            for sw in (swz_k, swz_v):
-                generic = r * D + 8 * (pc ^ sw(D, r))
-                lane_off = row0 * D + 8 * (pc0 ^ sw(D, row0))
-                assert np.array_equal(generic, lane_off + i * RPL * D)
-                for t in range(-(-S // KB)):
-                    k0 = t * KB
-                    if k0 + KB <= S:
-                        el = (k0 + i * RPL) * D + lane_off
-                    else:
-                        el = (np.minimum(k0 + r, S - 1) - row0) * D + lane_off
-                        ok = k0 + r < S
-                        assert np.array_equal(el[ok], (k0 * D + generic)[ok])
-                    assert el.min() >= 0 and (el + 8).max() <= S * D
-        # O and LSE stores
-        for qb in range(QB):
-            row = qw0[:, None] + 16 * qb + l16[None, :]
-            ok = row < S
-            if not ok.any():
-                continue
-            for db in range(DB):
-                off = bh[:, None] * S * D + row * D + 16 * db + 4 * g[None, :]
-                assert off[ok].min() >= 0 and (off[ok] + 4).max() <= total
-            lo = bh[:, None] * S + row
-            assert lo[ok].min() >= 0 and lo[ok].max() < B * H * S
+    bhs, qts = block_map(B * H, nqt, mode == "causal", group)
+    for bh, qt in zip(bhs.tolist(), qts.tolist()):
+        b, h = divmod(bh, H)
+        hk = h // group
+        start, ln = 0, S
+        if cu is not None:
+            s0 = min(max(cu[b], 0), total)
+            s1 = min(max(cu[b + 1], s0), total)
+            start, ln = s0, min(s1 - s0, S)
+        q0 = qt * BM
+        if q0 >= ln:
+            continue
+        qbase = b * q_sb + h * q_sh + start * q_sr
+        kvbase = b * kv_sb + hk * kv_sh + start * kv_sr
+        lbase = b * l_sb + h * l_sh + start
+        q_last = min(q0 + BM, ln) - 1
+        kbeg, kend = 0, ln
+        if mode == "causal":
+            kend = q_last + 1
+        if mode == "window":
+            kbeg, kend = max(0, q0 - wl), min(ln, q_last + wr + 1)
+        t_begin, t_end = kbeg // KB, -(-kend // KB)
+        for wave in range(NW):
+            qw0 = q0 + wave * QW
+            # Q loads (rows clamped to len-1, inside the sequence)
+            for qb in range(QB):
+                row = np.minimum(qw0 + 16 * qb + l16, ln - 1)
+                for kk in range(DK):
+                    off = qbase + row * q_sr + 32 * kk + 8 * g
+                    assert off.min() >= 0 and (off + 8).max() <= n_q
+                    assert (start + row).min() >= start and (start + row).max() < start + ln
+            # K/V direct-to-LDS loads: one lane offset per tensor, scalar steps
+            row0, pc0 = (wave * 64 + lane) // CPR, lane % CPR
+            for i in range(LOADS):
+                c = (i * NW + wave) * 64 + lane
+                r, pc = c // CPR, c % CPR
+                assert np.array_equal(r, row0 + i * RPL) and np.array_equal(pc, pc0)
+                dst = 2 * (i * NW + wave) * 512 + 16 * lane
+                assert dst.min() >= 0 and (dst + 16).max() <= 2 * LTILE
+                for sw in (swz_k, swz_v):
+                    lane_off = row0 * kv_sr + 8 * (pc0 ^ sw(D, row0))
+                    assert (2 * lane_off).max() < 2 ** 32
+                    for t in range(t_begin, t_end):
+                        k0 = t * KB
+                        if k0 + KB <= ln:
+                            el = kvbase + (k0 + i * RPL) * kv_sr + lane_off
+                            krow = k0 + r
+                        else:
+                            krow = np.minimum(k0 + r, ln - 1)
+                            el = kvbase + (krow - row0) * kv_sr + lane_off
+                        assert np.array_equal(el, kvbase + krow * kv_sr + 8 * (pc ^ sw(D, r)))
+                        assert el.min() >= 0 and (el + 8).max() <= n_kv
+                        assert krow.min() >= 0 and krow.max() < ln
+            # compute tiles this wave keeps, and the mask decision
+            kept_keys = set()
+            rows = np.arange(qw0, qw0 + QW)
+            valid = rows[rows < ln]
+            for t in range(t_begin, t_end):
+                for j in range(SUB):
+                    k0 = t * KB + j * BN
+                    if k0 >= kend:
+                        break
+                    if mode == "causal" and k0 > qw0 + QW - 1:
+                        break
+                    if mode == "window":
+                        if k0 > qw0 + QW - 1 + wr:
+                            break
+                        if k0 + BN - 1 < qw0 - wl:
+                            continue
+                    need = k0 + BN > ln
+                    if mode == "causal":
+                        need |= k0 + BN - 1 > qw0
+                    if mode == "window":
+                        need |= (k0 < qw0 + QW - 1 - wl) or (k0 + BN - 1 > qw0 + wr)
+                    keys = np.arange(k0, k0 + BN)
+                    if not need and valid.size:
+                        adm = (keys[None, :] < ln) & (keys[None, :] >= valid[:, None] - wl) & \
+                              (keys[None, :] <= valid[:, None] + wr)
+                        assert adm.all(), f"unmasked tile at key {k0} holds inadmissible keys"
+                    kept_keys.update(keys.tolist())
+            for i in valid.tolist():
+                adm = range(max(0, i - wl), min(ln - 1, i + wr) + 1)
+                missing = [k for k in adm if k not in kept_keys]
+                assert not missing, f"row {i}: admissible keys {missing[:4]} never computed"
+            # O and LSE stores
+            for qb in range(QB):
+                row = qw0 + 16 * qb + l16
+                ok = row < ln
+                if not ok.any():
+                    continue
+                for db in range(DB):
+                    off = qbase + row * q_sr + 16 * db + 4 * g
+                    assert off[ok].min() >= 0 and (off[ok] + 4).max() <= n_q
+                lo = lbase + row
+                assert lo[ok].min() >= 0 and lo[ok].max() < n_l
 
 
 @pytest.mark.parametrize("D", [64, 128])
@@ -197,3 +294,67 @@ def test_transposing_reads_match_the_score_layout(D):
                 for e in range(4):
                     assert np.array_equal(keys[:, e], 32 * kc + 16 * half + 4 * g + e)
                     assert np.array_equal(cols[:, e], 16 * db + l16)
+
+
+def _windows(S):
+    out = []
+    for wl, wr in ((0, 0), (1, 0), (3, 7), (64, 0), (100, 100), (255, 1), (0, 300), (S, 5), (7, S)):
+        out.append((min(wl, S), min(wr, S)))
+    return out
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("S", [1, 17, 64, 129, 300, 513, 1000])
+def test_window_coverage_and_bounds(D, S):
+    for window in _windows(S):
+        emulate(1, 2, S, D, False, window=window)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("H,H_kv", [(4, 4), (4, 2), (8, 1), (6, 3)])
+def test_gqa_bounds(D, H, H_kv):
+    for S in (65, 300):
+        for causal in (False, True):
+            emulate(2, H, S, D, causal, H_kv=H_kv)
+    emulate(1, H, 300, D, False, H_kv=H_kv, window=(20, 3))
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("lens", [[5, 0, 17, 1, 9], [256, 255, 257], [1000], [0, 0, 3], [513, 64, 700, 1]])
+def test_varlen_bounds(D, lens):
+    cu = np.concatenate([[0], np.cumsum(lens)]).tolist()
+    total = cu[-1]
+    S = max(1, max(lens))
+    for H, H_kv in ((2, 2), (4, 1)):
+        for causal in (False, True):
+            emulate(len(lens), H, S, D, causal, H_kv=H_kv, cu=cu, total=total)
+        emulate(len(lens), H, S, D, False, H_kv=H_kv, cu=cu, total=total, window=(min(30, S), 0))
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_malformed_sequence_tables_stay_in_bounds(D):
+    """Entries outside [0, total], decreasing entries and lengths beyond the
+    grid's longest sequence are clamped: no access leaves the tensors."""
+    total = 300
+    for cu, S in (([0, 500, 300], 300), ([-7, 100, 50, 300], 300), ([0, 300, 300], 64), ([10, 20, 400], 200),
+                  ([0, 2**31 - 1, -2**31], 300)):
+        emulate(len(cu) - 1, 2, S, D, False, cu=cu, total=total)
+        emulate(len(cu) - 1, 2, S, D, True, cu=cu, total=total)
+
+
+def test_dropout_counter_names_the_register_key():
+    """Element x of P^T register pb[qb][kc] of lane (l16, g) holds key
+    k0 + 32kc + 16(x//4) + 4g + x%4 (the S^T accumulator order). The kernel
+    draws it as word x%4 of the Philox call with first counter word
+    (k0 + 32kc + 16(x//4))/4 + g: the definition's (key // 4, word key % 4)."""
+    lane = np.arange(64)
+    g = lane >> 4
+    for k0 in (0, 64, 4096 - 64, 123 * 64):
+        for kc in range(2):
+            for x in range(8):
+                key = k0 + 32 * kc + 16 * (x // 4) + 4 * g + x % 4
+                half = x // 4
+                word = 2 * ((x % 4) // 2) + x % 2
+                jg = (k0 + 32 * kc + 16 * half) // 4 + g
+                assert np.array_equal(jg, key // 4) and word == x % 4
+                assert np.array_equal(key % 4, np.full(64, x % 4))
