@@ -158,8 +158,8 @@ def feature_setup(key: str, causal: bool, dev):
                                 seed=f.seed, rows=rows)
             secs = time.perf_counter() - t0
             i = rows % f.S
-            lo = np.maximum(0, i - wl) if wl >= 0 else 0
-            hi = np.minimum(f.S - 1, i + wr) if wr >= 0 else f.S - 1
+            lo = np.maximum(0, i - wl) if wl >= 0 else np.zeros_like(i)
+            hi = np.minimum(f.S - 1, i + wr) if wr >= 0 else np.full_like(i, f.S - 1)
             fl = float(np.sum(4.0 * f.D * (hi - lo + 1)))
             return fl, secs, f"every {stride}th query row ({len(rows)} of {f.B * f.H * f.S} rows)"
     cfg.update({"window": [wl, wr], "dropout_p": f.dropout_p, "causal": causal, "scale": f.scale,
