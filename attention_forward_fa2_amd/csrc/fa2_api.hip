@@ -96,6 +96,13 @@ int validate_varlen(const void* q, const void* k, const void* v, const void* o, 
         return FA2_ERR_ALIGN;
     if ((st = overflow_status((long long)num_seqs * H, max_seqlen, (long long)H_kv * D, D)) != FA2_OK) return st;
     if ((long long)H * D >= (1ll << 31)) return FA2_ERR_OVERFLOW;
+    {
+        // the packed grid rounds the (sequence, K/V head) units up to a multiple of 8
+        const fa2::TileShape ts = fa2::tile_shape(D);
+        const long long units8 = ((long long)num_seqs * H_kv + 7) / 8 * 8;
+        const long long nqt = (max_seqlen + ts.rows_per_block - 1) / ts.rows_per_block;
+        if (units8 * nqt * (H / H_kv) > 0x7fffffffll) return FA2_ERR_OVERFLOW;
+    }
     const size_t nq = (size_t)total * H * D * 2, nkv = (size_t)total * H_kv * D * 2, nl = (size_t)total * H * 4;
     return alias_status(q, nq, k, v, nkv, o, lse, nl, cu_seqlens, (size_t)(num_seqs + 1) * 4);
 }
@@ -181,7 +188,7 @@ extern "C" int fa2_kernel_config(int B, int H, int S, int D, int causal, int* ro
     int st = heads_status(H, H, D);
     if (st == FA2_OK) st = overflow_status((long long)B * H, S, D, D);
     if (st != FA2_OK) return st;
-    const fa2::TileShape ts = fa2::tile_shape(D);
+    const fa2::TileShape ts = fa2::dense_tile_shape(D, (long long)B * H, S, -1, causal ? 0 : -1);
     if (rows_per_block) *rows_per_block = ts.rows_per_block;
     if (keys_per_tile) *keys_per_tile = ts.keys_per_tile;
     if (threads_per_block) *threads_per_block = ts.threads;

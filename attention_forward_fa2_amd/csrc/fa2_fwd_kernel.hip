@@ -213,16 +213,32 @@ enum MaskKind { kNoMask = 0, kCausal = 1, kWindow = 2 };
 //    x, x+8, ... with all query heads of each, and walks them heaviest query
 //    tile first (the last tiles see the most keys), so the long workgroups
 //    start early and each K/V head has several tiles in flight on one XCD;
-//  * causal otherwise: heaviest tiles first over all heads.
+//  * causal otherwise: heaviest tiles first over all heads;
+//  * packed sequences of different lengths: (sequence, K/V head) unit u goes
+//    to XCD u mod 8, so that with 8 or more heads every XCD gets its share of
+//    every sequence whatever the lengths; an XCD walks its units one by one
+//    (all query tiles of a unit and all query heads of its group together;
+//    causal: heaviest tile first). The grid then has ceil(units/8)*8*nqt*group
+//    workgroups, and those past the last unit, or past the end of a short
+//    sequence, exit at once. Returns false for a workgroup with no work.
 template <int MASK>
-__device__ __forceinline__ void map_block(const KernelArgs& a, int bid, int& bh, int& qt) {
+__device__ __forceinline__ bool map_block(const KernelArgs& a, int bid, int& bh, int& qt) {
     const int xcd = bid & 7, slot = bid >> 3;
+    if (a.cu) {
+        const int per_unit = a.nqt * a.group;
+        const int kvu = xcd + 8 * (slot / per_unit);
+        const int rem = slot % per_unit;
+        qt = rem / a.group;
+        if (MASK == kCausal) qt = a.nqt - 1 - qt;
+        bh = kvu * a.group + rem % a.group;
+        return kvu < a.BHkv;
+    }
     if (MASK == kCausal && (a.BHkv & 7) == 0) {
         const int per_tile = (a.BHkv >> 3) * a.group;  // query heads per XCD
         qt = a.nqt - 1 - slot / per_tile;
         const int r = slot % per_tile;
         bh = (xcd + 8 * (r / a.group)) * a.group + r % a.group;
-        return;
+        return true;
     }
     const int per = a.nblocks >> 3, rem = a.nblocks & 7;
     const int logical = xcd * per + min(xcd, rem) + slot;
@@ -233,6 +249,7 @@ __device__ __forceinline__ void map_block(const KernelArgs& a, int bid, int& bh,
         bh = logical / a.nqt;
         qt = logical % a.nqt;
     }
+    return true;
 }
 
 // Philox4x32-10 (Salmon, Moraes, Dror and Shaw, "Parallel random numbers: as
@@ -265,6 +282,15 @@ __device__ __forceinline__ U32x4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_
 #ifndef FA2_SETPRIO
 #define FA2_SETPRIO 1
 #endif
+// 1: run the softmax check and the PV product per 32-key chunk (see compute_tile).
+#ifndef FA2_KC_SPLIT
+#define FA2_KC_SPLIT 0
+#endif
+// With the split: VALU instructions to interleave after each PV MFMA (0 = leave
+// the order to the compiler).
+#ifndef FA2_KC_SCHED
+#define FA2_KC_SCHED 0
+#endif
 
 template <class SH, int MASK, bool DROP>
 __global__ __launch_bounds__(SH::THREADS) __attribute__((amdgpu_waves_per_eu(SH::WAVES_PER_SIMD)))
@@ -285,7 +311,7 @@ void fa2_fwd_kernel(KernelArgs a) {
     const int bid = blockIdx.x + blockIdx.y * gridDim.x;  // grid is (x, y) only when x alone is too small
     if (bid >= a.nblocks) return;
     int bh, qt;
-    map_block<MASK>(a, bid, bh, qt);
+    if (!map_block<MASK>(a, bid, bh, qt)) return;
     const int b = bh / a.H, h = bh - b * a.H, hk = h / a.group;
 
     // This sequence's first row and length. A packed table is read with scalar
@@ -456,40 +482,165 @@ void fa2_fwd_kernel(KernelArgs a) {
         // p = 2^(s*c - m_run*c). l and o always use the same reference per row,
         // so O = o/l and LSE = scale*m_run + ln l hold for any reference; the
         // reference only has to keep every p representable in fp16. The
-        // common path therefore skips the tile max: it exponentiates against
-        // the current reference and accepts the tile if every lane's partial
+        // common path therefore skips the row max: it exponentiates against
+        // the current reference and accepts the result if every lane's partial
         // row sum of the fp16 p stays below 2^15 (so no p overflowed). The
-        // first tile, or a tile that fails the check, takes the row max of the
-        // tile (combined over the 4 lanes of a query), moves the reference to
-        // max(m_run, tile max), rescales o and l by alpha = 2^((m_old - m_new)*c)
+        // first tile, or a chunk that fails the check, takes the row max
+        // (combined over the 4 lanes of a query), moves the reference to
+        // max(m_run, max), rescales o and l by alpha = 2^((m_old - m_new)*c)
         // and exponentiates again: the update of the online softmax.
         half8 pb[QB][NKC];
-        float rs[QB];
-        auto exponentiate = [&]() {
+
+        // p of 32-key chunk kc (16-key blocks 2kc, 2kc+1) of query block qb, as
+        // the fp16 B operand of the PV product, and its partial row sum (over
+        // the fp16 values, before dropout: the softmax normaliser counts every
+        // admissible key).
+        auto exp_chunk = [&](int qb, int kc, float& rsum) __attribute__((always_inline)) {
+            const float mc = m_run[qb] * a.c;
+            const f32x4 lo = sacc[qb][2 * kc], hi = sacc[qb][2 * kc + 1];
+            half2 h[4];
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(lo[2 * e], a.c, -mc));
+                const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(lo[2 * e + 1], a.c, -mc));
+                const float p2 = __builtin_amdgcn_exp2f(__builtin_fmaf(hi[2 * e], a.c, -mc));
+                const float p3 = __builtin_amdgcn_exp2f(__builtin_fmaf(hi[2 * e + 1], a.c, -mc));
+                h[e] = half2{(_Float16)p0, (_Float16)p1};
+                h[2 + e] = half2{(_Float16)p2, (_Float16)p3};
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) rsum = __builtin_amdgcn_fdot2(h[e], kOnes2, rsum, false);
+            pb[qb][kc] = half8{h[0][0], h[0][1], h[1][0], h[1][1], h[2][0], h[2][1], h[3][0], h[3][1]};
+        };
+        // Row max over 16-key blocks kb0 .. kb1-1, combined over the 4 lanes of a query.
+        auto row_max = [&](int qb, int kb0, int kb1) __attribute__((always_inline)) {
+            float a0 = fmaxf(sacc[qb][kb0][0], sacc[qb][kb0][1]);
+            float a1 = fmaxf(sacc[qb][kb0][2], sacc[qb][kb0][3]);
+            for (int kb = kb0 + 1; kb < kb1; ++kb) {
+                a0 = fmaxf(a0, fmaxf(sacc[qb][kb][0], sacc[qb][kb][1]));
+                a1 = fmaxf(a1, fmaxf(sacc[qb][kb][2], sacc[qb][kb][3]));
+            }
+            return max_xor32(max_xor16(fmaxf(a0, a1)));
+        };
+        // Move the reference of query block qb up to mx (if higher), rescaling o and l.
+        auto move_reference = [&](int qb, float mx) __attribute__((always_inline)) {
+            const float m_new = fmaxf(m_run[qb], mx);
+            const float alpha = __builtin_amdgcn_exp2f((m_run[qb] - m_new) * a.c);
+            m_run[qb] = m_new;
+            l_run[qb] *= alpha;
+#pragma unroll
+            for (int db = 0; db < DB; ++db) oacc[db][qb] *= alpha;
+        };
+
+        // ---- dropout on P: zero the probabilities of dropped keys ----
+        // Key j of query row i (both within the sequence) of head (b, h) draws
+        // word j%4 of Philox4x32-10 at counter (j/4, i, b*H + h, offset) under
+        // key (seed_lo, seed_hi), and is kept when that word is >= drop_thr. A
+        // lane's 4 keys of a 16-key block are 4 consecutive keys starting at a
+        // multiple of 4, i.e. one Philox call. Kept probabilities are scaled by
+        // 1/(1-p) in the epilogue.
+        auto drop_chunk = [&](int kc) __attribute__((always_inline)) {
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb) {
-                const float mc = m_run[qb] * a.c;
-                float acc = 0.f;
+                const uint32_t qrow = (uint32_t)(qw0 + 16 * qb + l16);
+                uint32_t m[4];
 #pragma unroll
-                for (int kc = 0; kc < NKC; ++kc) {
-                    const f32x4 lo = sacc[qb][2 * kc], hi = sacc[qb][2 * kc + 1];
-                    half2 h[4];
-#pragma unroll
-                    for (int e = 0; e < 2; ++e) {
-                        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(lo[2 * e], a.c, -mc));
-                        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(lo[2 * e + 1], a.c, -mc));
-                        const float p2 = __builtin_amdgcn_exp2f(__builtin_fmaf(hi[2 * e], a.c, -mc));
-                        const float p3 = __builtin_amdgcn_exp2f(__builtin_fmaf(hi[2 * e + 1], a.c, -mc));
-                        h[e] = half2{(_Float16)p0, (_Float16)p1};
-                        h[2 + e] = half2{(_Float16)p2, (_Float16)p3};
-                    }
-                    // row sum over the fp16 probabilities (before dropout: the
-                    // softmax normaliser counts every admissible key)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_fdot2(h[e], kOnes2, acc, false);
-                    pb[qb][kc] = half8{h[0][0], h[0][1], h[1][0], h[1][1], h[2][0], h[2][1], h[3][0], h[3][1]};
+                for (int half_ = 0; half_ < 2; ++half_) {
+                    const uint32_t jg = (uint32_t)((k0 + 32 * kc + 16 * half_) >> 2) + (uint32_t)g;
+                    const U32x4 r = philox4x32_10(jg, qrow, (uint32_t)bh, a.offset, a.seed_lo, a.seed_hi);
+                    m[2 * half_ + 0] = (r.w[0] >= a.drop_thr ? 0x0000FFFFu : 0u) |
+                                       (r.w[1] >= a.drop_thr ? 0xFFFF0000u : 0u);
+                    m[2 * half_ + 1] = (r.w[2] >= a.drop_thr ? 0x0000FFFFu : 0u) |
+                                       (r.w[3] >= a.drop_thr ? 0xFFFF0000u : 0u);
                 }
-                rs[qb] = acc;
+                typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+                u32x4v bits = __builtin_bit_cast(u32x4v, pb[qb][kc]);
+                bits &= u32x4v{m[0], m[1], m[2], m[3]};
+                pb[qb][kc] = __builtin_bit_cast(half8, bits);
+            }
+        };
+
+        // ---- O^T += V^T P^T on MFMA, for 32-key chunk kc ----
+        // Source lane l16 of group g points at row 4g + l16/4 (+16 for the second
+        // half) and columns 16*db + 4*(l16%4) .. +3; the transposing read returns
+        // V[32kc + 4g + e][16db + l16] in element e.
+        auto pv_chunk = [&](int kc) __attribute__((always_inline)) {
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                const char* p0 = ldsV + rdV[db] + kc * 32 * D * 2;
+                const s16x4 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p0);
+                const s16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0 + 16 * D * 2));
+                const half4 h0 = __builtin_bit_cast(half4, t0);
+                const half4 h1 = __builtin_bit_cast(half4, t1);
+                const half8 va = half8{h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb)
+                    oacc[db][qb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb[qb][kc], oacc[db][qb], 0, 0, 0);
+            }
+        };
+
+#if FA2_KC_SPLIT
+        // Chunk by chunk: the check, and if needed the reference move, are done
+        // per 32-key chunk, so the PV product of chunk kc and the
+        // exponentials of chunk kc+1 share a basic block and can overlap in
+        // the wave's instruction stream. A reference move after chunk kc has
+        // been accumulated rescales it with the rest of o, as for any tile.
+        if (fresh) {
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) move_reference(qb, row_max(qb, 0, NKB));
+        }
+#pragma unroll
+        for (int kc = 0; kc < NKC; ++kc) {
+            float rs[QB];
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) {
+                rs[qb] = 0.f;
+                exp_chunk(qb, kc, rs[qb]);
+            }
+#if FA2_KC_SCHED
+            if (kc > 0) {
+                // This basic block also holds the PV product of chunk kc-1:
+                // alternate its MFMAs with the exponentials of chunk kc so the
+                // wave issues VALU work while the matrix unit is busy.
+                __builtin_amdgcn_sched_group_barrier(0x100, DB, 0);  // V reads of the first half
+#pragma unroll
+                for (int i = 0; i < DB * QB; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);          // one MFMA
+                    __builtin_amdgcn_sched_group_barrier(0x002, FA2_KC_SCHED, 0);  // VALU
+                    if (i == DB * QB / 2 - 1) __builtin_amdgcn_sched_group_barrier(0x100, DB, 0);
+                }
+            }
+#endif
+            if (!fresh) {
+                bool over = false;
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb) over |= !(rs[qb] < kSpeculateLimit);
+                if (__builtin_amdgcn_ballot_w64(over) != 0) {  // wave-uniform
+#pragma unroll
+                    for (int qb = 0; qb < QB; ++qb) {
+                        move_reference(qb, row_max(qb, 2 * kc, 2 * kc + 2));
+                        rs[qb] = 0.f;
+                        exp_chunk(qb, kc, rs[qb]);
+                    }
+                }
+            }
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) l_run[qb] += rs[qb];
+            if (DROP) drop_chunk(kc);
+            if (FA2_SETPRIO) __builtin_amdgcn_s_setprio(1);
+            pv_chunk(kc);
+            if (FA2_SETPRIO) __builtin_amdgcn_s_setprio(0);
+        }
+        fresh = false;
+#else
+        // Whole tile at once: exponentiate every chunk, one check per tile.
+        float rs[QB];
+        auto exponentiate = [&]() __attribute__((always_inline)) {
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) {
+                rs[qb] = 0.f;
+#pragma unroll
+                for (int kc = 0; kc < NKC; ++kc) exp_chunk(qb, kc, rs[qb]);
             }
         };
         bool move_ref = fresh;
@@ -502,80 +653,21 @@ void fa2_fwd_kernel(KernelArgs a) {
         }
         if (move_ref) {
 #pragma unroll
-            for (int qb = 0; qb < QB; ++qb) {
-                float a0 = fmaxf(sacc[qb][0][0], sacc[qb][0][1]);
-                float a1 = fmaxf(sacc[qb][0][2], sacc[qb][0][3]);
-#pragma unroll
-                for (int kb = 1; kb < NKB; ++kb) {
-                    a0 = fmaxf(a0, fmaxf(sacc[qb][kb][0], sacc[qb][kb][1]));
-                    a1 = fmaxf(a1, fmaxf(sacc[qb][kb][2], sacc[qb][kb][3]));
-                }
-                const float mx = max_xor32(max_xor16(fmaxf(a0, a1)));
-                const float m_new = fmaxf(m_run[qb], mx);
-                const float alpha = __builtin_amdgcn_exp2f((m_run[qb] - m_new) * a.c);
-                m_run[qb] = m_new;
-                l_run[qb] *= alpha;
-#pragma unroll
-                for (int db = 0; db < DB; ++db) oacc[db][qb] *= alpha;
-            }
+            for (int qb = 0; qb < QB; ++qb) move_reference(qb, row_max(qb, 0, NKB));
             exponentiate();
         }
         fresh = false;
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) l_run[qb] += rs[qb];
-
-        // ---- dropout on P: zero the probabilities of dropped keys ----
-        // Key j of query row i (both within the sequence) of head (b, h) draws
-        // word j%4 of Philox4x32-10 at counter (j/4, i, b*H + h, offset) under
-        // key (seed_lo, seed_hi), and is kept when that word is >= drop_thr. A
-        // lane's 4 keys of a 16-key block are 4 consecutive keys starting at a
-        // multiple of 4, i.e. one Philox call. Kept probabilities are scaled by
-        // 1/(1-p) in the epilogue.
         if (DROP) {
 #pragma unroll
-            for (int qb = 0; qb < QB; ++qb) {
-                const uint32_t qrow = (uint32_t)(qw0 + 16 * qb + l16);
-#pragma unroll
-                for (int kc = 0; kc < NKC; ++kc) {
-                    uint32_t m[4];
-#pragma unroll
-                    for (int half_ = 0; half_ < 2; ++half_) {
-                        const uint32_t jg = (uint32_t)((k0 + 32 * kc + 16 * half_) >> 2) + (uint32_t)g;
-                        const U32x4 r = philox4x32_10(jg, qrow, (uint32_t)bh, a.offset, a.seed_lo, a.seed_hi);
-                        m[2 * half_ + 0] = (r.w[0] >= a.drop_thr ? 0x0000FFFFu : 0u) |
-                                           (r.w[1] >= a.drop_thr ? 0xFFFF0000u : 0u);
-                        m[2 * half_ + 1] = (r.w[2] >= a.drop_thr ? 0x0000FFFFu : 0u) |
-                                           (r.w[3] >= a.drop_thr ? 0xFFFF0000u : 0u);
-                    }
-                    typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
-                    u32x4v bits = __builtin_bit_cast(u32x4v, pb[qb][kc]);
-                    bits &= u32x4v{m[0], m[1], m[2], m[3]};
-                    pb[qb][kc] = __builtin_bit_cast(half8, bits);
-                }
-            }
+            for (int kc = 0; kc < NKC; ++kc) drop_chunk(kc);
         }
-
-        // ---- O^T += V^T P^T on MFMA ----
-        // Source lane l16 of group g points at row 4g + l16/4 (+16 for the second
-        // half) and columns 16*db + 4*(l16%4) .. +3; the transposing read returns
-        // V[32kc + 4g + e][16db + l16] in element e.
         if (FA2_SETPRIO) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
-#pragma unroll
-            for (int kc = 0; kc < NKC; ++kc) {
-                const char* p0 = ldsV + rdV[db] + kc * 32 * D * 2;
-                const s16x4 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p0);
-                const s16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0 + 16 * D * 2));
-                const half4 h0 = __builtin_bit_cast(half4, t0);
-                const half4 h1 = __builtin_bit_cast(half4, t1);
-                const half8 va = half8{h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
-#pragma unroll
-                for (int qb = 0; qb < QB; ++qb)
-                    oacc[db][qb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb[qb][kc], oacc[db][qb], 0, 0, 0);
-            }
-        }
+        for (int kc = 0; kc < NKC; ++kc) pv_chunk(kc);
         if (FA2_SETPRIO) __builtin_amdgcn_s_setprio(0);
+#endif
     };
 
     // One step of the scan over ring stage t (SUB compute tiles) held in stage ST.
@@ -659,6 +751,31 @@ void fa2_fwd_kernel(KernelArgs a) {
 #endif
 using Shape64 = Shape<64, FA2_D64_QB, FA2_D64_NW, FA2_D64_BN, FA2_D64_SUB>;
 using Shape128 = Shape<128, FA2_D128_QB, FA2_D128_NW, FA2_D128_BN, FA2_D128_SUB>;
+// Half-height workgroups (4 waves, 128 query rows, one compute tile per ring
+// stage) for causal launches whose full-height grid fits in one round of
+// resident workgroups: there every workgroup starts at once and the launch
+// lasts as long as its heaviest (diagonal-most) workgroup, which halving the
+// workgroup height halves. Larger causal grids are balanced by the
+// heaviest-first order and keep the full-height tiles.
+using Shape64c = Shape<64, FA2_D64_QB, 4, FA2_D64_BN, 1>;
+using Shape128c = Shape<128, FA2_D128_QB, 4, FA2_D128_BN, 1>;
+
+constexpr int kCUs = 256;                 // MI355X compute units
+constexpr int kLdsPerCU = 160 * 1024;     // LDS bytes per compute unit
+
+// Workgroups of shape SH resident per compute unit (LDS and register limits).
+template <class SH>
+constexpr int wg_per_cu() {
+    return (kLdsPerCU / SH::LDS_BYTES) < (SH::WAVES_PER_SIMD * 4 / SH::NW) ? (kLdsPerCU / SH::LDS_BYTES)
+                                                                           : (SH::WAVES_PER_SIMD * 4 / SH::NW);
+}
+#ifndef FA2_SMALL_CAUSAL
+#define FA2_SMALL_CAUSAL 1
+#endif
+template <class SH>
+bool fits_one_round(long long units, int S) {
+    return FA2_SMALL_CAUSAL && units * ((S + SH::BM - 1) / SH::BM) <= (long long)kCUs * wg_per_cu<SH>();
+}
 
 constexpr int kMaxDevices = 64;
 
@@ -726,7 +843,7 @@ hipError_t launch_d(const LaunchArgs& a, hipStream_t stream) {
     k.BH = a.B * a.H;
     k.BHkv = a.B * a.H_kv;
     k.nqt = (a.S + SH::BM - 1) / SH::BM;
-    k.nblocks = k.BH * k.nqt;
+    k.nblocks = a.cu_seqlens ? ((k.BHkv + 7) / 8) * 8 * k.nqt * k.group : k.BH * k.nqt;
     k.c = (float)((double)a.scale * kLog2e);
 
     // Window: a negative or out-of-range side is unbounded (S keys).
@@ -757,9 +874,21 @@ hipError_t launch_d(const LaunchArgs& a, hipStream_t stream) {
 
 }  // namespace
 
-TileShape tile_shape(int D) {
-    if (D == 128) return {Shape128::BM, Shape128::KB, Shape128::THREADS, Shape128::LDS_BYTES};
-    return {Shape64::BM, Shape64::KB, Shape64::THREADS, Shape64::LDS_BYTES};
+template <class SH>
+TileShape describe() {
+    return {SH::BM, SH::KB, SH::THREADS, SH::LDS_BYTES};
+}
+
+TileShape tile_shape(int D) { return D == 128 ? describe<Shape128>() : describe<Shape64>(); }
+
+// A dense launch is causal when the left side of the window is open and the
+// right side is 0 (the rule launch_d applies).
+static bool causal_window(int S, int wl, int wr) { return (wl < 0 || wl >= S) && wr == 0; }
+
+TileShape dense_tile_shape(int D, long long units, int S, int window_left, int window_right) {
+    const bool c = causal_window(S, window_left, window_right);
+    if (D == 128) return (c && fits_one_round<Shape128>(units, S)) ? describe<Shape128c>() : describe<Shape128>();
+    return (c && fits_one_round<Shape64>(units, S)) ? describe<Shape64c>() : describe<Shape64>();
 }
 
 uint32_t drop_threshold(float p) {
@@ -769,8 +898,13 @@ uint32_t drop_threshold(float p) {
 }
 
 hipError_t launch_forward(const LaunchArgs& a, hipStream_t stream) {
-    if (a.D == 64) return launch_d<Shape64>(a, stream);
-    return launch_d<Shape128>(a, stream);
+    const long long units = (long long)a.B * a.H;
+    const bool small = !a.cu_seqlens && causal_window(a.S, a.window_left, a.window_right);
+    if (a.D == 64)
+        return (small && fits_one_round<Shape64>(units, a.S)) ? launch_d<Shape64c>(a, stream)
+                                                               : launch_d<Shape64>(a, stream);
+    return (small && fits_one_round<Shape128>(units, a.S)) ? launch_d<Shape128c>(a, stream)
+                                                           : launch_d<Shape128>(a, stream);
 }
 
 }  // namespace fa2

@@ -13,8 +13,13 @@ struct TileShape {
     int lds_bytes;        // dynamic LDS per workgroup
 };
 
-// Shape used for head dimension D (64 or 128).
+// The full-height shape for head dimension D (64 or 128); every other shape
+// has fewer rows per workgroup only when the full-height grid is small, so
+// this one bounds the grid size.
 TileShape tile_shape(int D);
+
+// The shape a dense launch of `units` (batch*head) heads of length S uses.
+TileShape dense_tile_shape(int D, long long units, int S, int window_left, int window_right);
 
 // Already-validated arguments of one forward pass.
 struct LaunchArgs {

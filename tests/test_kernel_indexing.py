@@ -38,6 +38,38 @@ SHAPES = {64: (2, 8, 64, 2), 128: (2, 8, 64, 2)}
 VARIANTS = [(2, 8, 64, 1), (2, 8, 64, 2), (2, 4, 64, 1), (2, 4, 64, 2), (4, 4, 64, 1)]
 
 
+def block_map_packed(BH, nqt, causal, group=1):
+    """Packed sequences: (sequence, K/V head) unit u on XCD u mod 8, unit by
+    unit. Returns (bh, qt, valid) over the padded grid."""
+    BHkv = BH // group
+    nb = -(-BHkv // 8) * 8 * nqt * group
+    bid = np.arange(nb)
+    xcd, slot = bid & 7, bid >> 3
+    per_unit = nqt * group
+    kvu = xcd + 8 * (slot // per_unit)
+    rem = slot % per_unit
+    qt = rem // group
+    if causal:
+        qt = nqt - 1 - qt
+    return kvu * group + rem % group, qt, kvu < BHkv
+
+
+@pytest.mark.parametrize("BHkv", [1, 3, 8, 12, 24, 40])
+@pytest.mark.parametrize("group", [1, 2, 4])
+@pytest.mark.parametrize("nqt", [1, 3, 16])
+@pytest.mark.parametrize("causal", [False, True])
+def test_packed_mapping(BHkv, group, nqt, causal):
+    """Every (unit, query tile) exactly once among the valid workgroups, each
+    K/V unit's workgroups on XCD unit mod 8."""
+    BH = BHkv * group
+    bh, qt, ok = block_map_packed(BH, nqt, causal, group)
+    bh, qt = bh[ok], qt[ok]
+    assert bh.min() >= 0 and bh.max() < BH and qt.min() >= 0 and qt.max() < nqt
+    assert len(set(zip(bh.tolist(), qt.tolist()))) == BH * nqt == ok.sum()
+    xcd = np.nonzero(ok)[0] & 7
+    assert np.array_equal(xcd, (bh // group) % 8)
+
+
 def block_map(BH, nqt, causal, group=1):
     nb = BH * nqt
     bid = np.arange(nb)
@@ -110,7 +142,12 @@ def emulate(B, H, S, D, causal, shape=None, H_kv=None, cu=None, total=None, wind
     lane = np.arange(64)
     l16, g = lane & 15, lane >> 4
     nqt = -(-S // BM)
-    bhs, qts = block_map(B * H, nqt, mode == "causal", group)
+    if cu is None:
+        bhs, qts = block_map(B * H, nqt, mode == "causal", group)
+    else:
+        bhs, qts, valid = block_map_packed(B * H, nqt, mode == "causal", group)
+        bhs, qts = bhs[valid], qts[valid]
+        assert len(set(zip(bhs.tolist(), qts.tolist()))) == B * H * nqt
     for bh, qt in zip(bhs.tolist(), qts.tolist()):
         b, h = divmod(bh, H)
         hk = h // group

@@ -206,3 +206,20 @@ def test_full_size_sampled(cid, causal):
     vmax = v.max(axis=2, keepdims=True).astype(np.float32)
     O32 = O.astype(np.float32)
     assert np.all(O32 >= vmin - 2e-3) and np.all(O32 <= vmax + 2e-3)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_reference_moves_in_some_workgroups_only(D):
+    """Heads 0 and 2 have scores rising by about 2.9 (base 2) per key, so their
+    running reference must move on every tile; heads 1 and 3 are ordinary and
+    almost never move it. Both kinds of workgroup run side by side in one
+    launch; all results must match the oracle."""
+    S = 1000
+    q, k, v = make_random(43_000 + D, 1, 4, S, D)
+    for h in (0, 2):
+        q[0, h] = 0
+        k[0, h] = 0
+        q[0, h, :, 0] = 4.0
+        k[0, h, :, 0] = (np.arange(S) * 0.5).astype(np.float16)
+    for causal in (False, True):
+        full_case(q, k, v, causal, 1.0 / math.sqrt(D) if D == 64 else 0.125, f"mixed reference moves D={D}")
