@@ -265,8 +265,9 @@ __device__ __forceinline__ U32x4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_
     for (int r = 0; r < 10; ++r) {
         const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
         const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
-        const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
-        const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+        // three-input xor in one v_bitop3_b32 (truth table 0x96 = a ^ b ^ c)
+        const uint32_t n0 = __builtin_amdgcn_bitop3_b32((uint32_t)(p1 >> 32), c1, k0, 0x96);
+        const uint32_t n2 = __builtin_amdgcn_bitop3_b32((uint32_t)(p0 >> 32), c3, k1, 0x96);
         c1 = (uint32_t)p1;
         c3 = (uint32_t)p0;
         c0 = n0;
@@ -281,6 +282,10 @@ __device__ __forceinline__ U32x4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_
 // unit fed from whichever wave has MFMAs ready (a scheduling hint only).
 #ifndef FA2_SETPRIO
 #define FA2_SETPRIO 1
+#endif
+// 16-key blocks whose score MFMAs are interleaved (1, 2 or 4; see compute_tile).
+#ifndef FA2_QK_GROUP
+#define FA2_QK_GROUP 4
 #endif
 // 1: run the softmax check and the PV product per 32-key chunk (see compute_tile).
 #ifndef FA2_KC_SPLIT
@@ -443,14 +448,20 @@ void fa2_fwd_kernel(KernelArgs a) {
         for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) sacc[qb][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        // The k-steps of one 16-key block accumulate into the same registers;
+        // FA2_QK_GROUP blocks are interleaved so that dependent MFMAs are
+        // 2*FA2_QK_GROUP-1 independent ones apart.
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
+        for (int kb0 = 0; kb0 < NKB; kb0 += FA2_QK_GROUP) {
 #pragma unroll
             for (int kk = 0; kk < DK; ++kk) {
-                const half8 ka = *reinterpret_cast<const half8*>(ldsK + rdK[kk] + kb * 16 * D * 2);
 #pragma unroll
-                for (int qb = 0; qb < QB; ++qb)
-                    sacc[qb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qreg[qb][kk], sacc[qb][kb], 0, 0, 0);
+                for (int kb = kb0; kb < kb0 + FA2_QK_GROUP; ++kb) {
+                    const half8 ka = *reinterpret_cast<const half8*>(ldsK + rdK[kk] + kb * 16 * D * 2);
+#pragma unroll
+                    for (int qb = 0; qb < QB; ++qb)
+                        sacc[qb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qreg[qb][kk], sacc[qb][kb], 0, 0, 0);
+                }
             }
         }
         if (FA2_SETPRIO) __builtin_amdgcn_s_setprio(0);
