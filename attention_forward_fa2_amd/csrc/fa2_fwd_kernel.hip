@@ -287,6 +287,12 @@ __device__ __forceinline__ U32x4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_
 #ifndef FA2_QK_GROUP
 #define FA2_QK_GROUP 4
 #endif
+// Row sums of P on the matrix unit (an MFMA against an all-ones operand)
+// instead of v_dot2 on the VALU: 0 never, 1 always, 2 for D=128 and for
+// unmasked D=64 (where it measured faster; elsewhere it was even or slower).
+#ifndef FA2_MFMA_ROWSUM
+#define FA2_MFMA_ROWSUM 2
+#endif
 // 1: run the softmax check and the PV product per 32-key chunk (see compute_tile).
 #ifndef FA2_KC_SPLIT
 #define FA2_KC_SPLIT 0
@@ -303,6 +309,8 @@ void fa2_fwd_kernel(KernelArgs a) {
     constexpr int D = SH::D, QB = SH::QB, NW = SH::NW, BN = SH::BN, QW = SH::QW, BM = SH::BM;
     constexpr int NKB = SH::NKB, NKC = SH::NKC, DK = SH::DK, DB = SH::DB, CPR = SH::CPR;
     constexpr int TILE = SH::TILE, LTILE = SH::LTILE, LOADS = SH::LOADS, SUB = SH::SUB, KB = SH::KB;
+    constexpr bool ROWSUM_MFMA =
+        !FA2_KC_SPLIT && (FA2_MFMA_ROWSUM == 1 || (FA2_MFMA_ROWSUM == 2 && (D == 128 || MASK == kNoMask)));
 
     // LDS ring: [stage][K | V][LTILE] halves; a stage holds SUB compute tiles.
     extern __shared__ __attribute__((aligned(16))) _Float16 smem[];
@@ -419,6 +427,10 @@ void fa2_fwd_kernel(KernelArgs a) {
         l_run[qb] = 0.f;
     }
     const half2 kOnes2 = half2{(_Float16)1.0f, (_Float16)1.0f};
+    // All-ones A operand: an MFMA with it sums the B operand (P^T) over its
+    // 32 keys, giving every lane its query's row sum.
+    const half8 kOnes8 = half8{(_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f,
+                               (_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f};
     bool fresh = true;  // no tile computed by this wave yet
 
     // LDS read offsets (bytes) that do not depend on the tile: the K swizzle of
@@ -494,8 +506,9 @@ void fa2_fwd_kernel(KernelArgs a) {
         // so O = o/l and LSE = scale*m_run + ln l hold for any reference; the
         // reference only has to keep every p representable in fp16. The
         // common path therefore skips the row max: it exponentiates against
-        // the current reference and accepts the result if every lane's partial
-        // row sum of the fp16 p stays below 2^15 (so no p overflowed). The
+        // the current reference and accepts the result if the row sum of the
+        // fp16 p (a lane's partial sum, or with the matrix-unit sums the
+        // tile's full row sum) stays below 2^15, so no p overflowed. The
         // first tile, or a chunk that fails the check, takes the row max
         // (combined over the 4 lanes of a query), moves the reference to
         // max(m_run, max), rescales o and l by alpha = 2^((m_old - m_new)*c)
@@ -519,8 +532,10 @@ void fa2_fwd_kernel(KernelArgs a) {
                 h[e] = half2{(_Float16)p0, (_Float16)p1};
                 h[2 + e] = half2{(_Float16)p2, (_Float16)p3};
             }
+            if (!ROWSUM_MFMA) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) rsum = __builtin_amdgcn_fdot2(h[e], kOnes2, rsum, false);
+                for (int e = 0; e < 4; ++e) rsum = __builtin_amdgcn_fdot2(h[e], kOnes2, rsum, false);
+            }
             pb[qb][kc] = half8{h[0][0], h[0][1], h[1][0], h[1][1], h[2][0], h[2][1], h[3][0], h[3][1]};
         };
         // Row max over 16-key blocks kb0 .. kb1-1, combined over the 4 lanes of a query.
@@ -653,6 +668,18 @@ void fa2_fwd_kernel(KernelArgs a) {
 #pragma unroll
                 for (int kc = 0; kc < NKC; ++kc) exp_chunk(qb, kc, rs[qb]);
             }
+            if (ROWSUM_MFMA) {
+                // the tile's full row sums on the matrix unit (each lane gets
+                // its query's sum over all BN keys)
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb) {
+                    f32x4 ls = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int kc = 0; kc < NKC; ++kc)
+                        ls = __builtin_amdgcn_mfma_f32_16x16x32_f16(kOnes8, pb[qb][kc], ls, 0, 0, 0);
+                    rs[qb] = ls[0];
+                }
+            }
         };
         bool move_ref = fresh;
         if (!move_ref) {
@@ -716,8 +743,10 @@ void fa2_fwd_kernel(KernelArgs a) {
     float* __restrict__ Lh = a.lse + b * a.l_sb + h * a.l_sh + start;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-        float lt = sum_xor16(l_run[qb]);
-        lt = sum_xor32(lt);
+        // l_run holds per-lane partial sums (4 lanes per query) unless the row
+        // sums come from the matrix unit, where every lane has the full sum.
+        float lt = l_run[qb];
+        if (!ROWSUM_MFMA) lt = sum_xor32(sum_xor16(lt));
         const float inv = (DROP ? a.out_scale : 1.0f) / lt;
         const int row = qw0 + 16 * qb + l16;
         if (row < len) {
