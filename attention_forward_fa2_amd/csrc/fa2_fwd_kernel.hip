@@ -303,8 +303,15 @@ __device__ __forceinline__ U32x4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_
 #define FA2_KC_SCHED 0
 #endif
 
+// Occupancy target of the dropout instances at D=64 (waves per SIMD); the
+// generator's registers do not fit the 4-wave budget without spills.
+#ifndef FA2_DROP_WAVES
+#define FA2_DROP_WAVES 4
+#endif
+
 template <class SH, int MASK, bool DROP>
-__global__ __launch_bounds__(SH::THREADS) __attribute__((amdgpu_waves_per_eu(SH::WAVES_PER_SIMD)))
+__global__ __launch_bounds__(SH::THREADS)
+__attribute__((amdgpu_waves_per_eu((DROP && SH::D == 64) ? FA2_DROP_WAVES : SH::WAVES_PER_SIMD)))
 void fa2_fwd_kernel(KernelArgs a) {
     constexpr int D = SH::D, QB = SH::QB, NW = SH::NW, BN = SH::BN, QW = SH::QW, BM = SH::BM;
     constexpr int NKB = SH::NKB, NKC = SH::NKC, DK = SH::DK, DB = SH::DB, CPR = SH::CPR;
@@ -427,31 +434,30 @@ void fa2_fwd_kernel(KernelArgs a) {
         l_run[qb] = 0.f;
     }
     const half2 kOnes2 = half2{(_Float16)1.0f, (_Float16)1.0f};
-    // All-ones A operand: an MFMA with it sums the B operand (P^T) over its
-    // 32 keys, giving every lane its query's row sum.
-    const half8 kOnes8 = half8{(_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f,
-                               (_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f};
     bool fresh = true;  // no tile computed by this wave yet
 
     // LDS read offsets (bytes) that do not depend on the tile: the K swizzle of
     // rows 16*kb + l16 depends on l16 only, the V swizzle of rows
-    // 32*kc + 4g + l16/4 (+16) on g and l16 only.
-    uint32_t rdK[DK];
-#pragma unroll
-    for (int kk = 0; kk < DK; ++kk) rdK[kk] = 2u * (l16 * D + 8 * ((4 * kk + g) ^ swz_k<D>(l16)));
-    uint32_t rdV[DB];
-    {
+    // 32*kc + 4g + l16/4 (+16) on g and l16 only. The k-step kk (K) and the
+    // column block db (V) only flip the address bits the swizzle acts on,
+    // which the row and lane terms leave clear, so
+    //   offset(K, kk) = rdK0 ^ (kk << 6),   offset(V, db) = rdV0 ^ (db << 5):
+    // one register per tensor instead of one per k-step or column block.
+    const uint32_t rdK0 = 2u * (l16 * D + 8 * (g ^ swz_k<D>(l16)));
+    const uint32_t rdV0 = [&] {
         const int r0 = 4 * g + (l16 >> 2);
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-            const int lc = 2 * db + ((l16 & 3) >> 1);
-            rdV[db] = 2u * (r0 * D + 8 * (lc ^ swz_v<D>(r0)) + 4 * (l16 & 1));
-        }
-    }
+        return 2u * (r0 * D + 8 * (((l16 & 3) >> 1) ^ swz_v<D>(r0)) + 4 * (l16 & 1));
+    }();
 
     // One compute tile: keys k0 .. k0+BN-1, K and V at the given LDS addresses.
     auto compute_tile = [&](const int k0, const char* const ldsK, const char* const ldsV)
                             __attribute__((always_inline)) {
+
+        // The per-k-step and per-column-block offsets are derived from the two
+        // bases inside the tile; the empty asm keeps the compiler from
+        // hoisting them out of the loop into registers of their own.
+        uint32_t rk = rdK0, rv = rdV0;
+        asm volatile("" : "+v"(rk), "+v"(rv));
 
         // ---- S^T = K Q^T on MFMA ----
         if (FA2_SETPRIO) __builtin_amdgcn_s_setprio(1);
@@ -469,7 +475,7 @@ void fa2_fwd_kernel(KernelArgs a) {
             for (int kk = 0; kk < DK; ++kk) {
 #pragma unroll
                 for (int kb = kb0; kb < kb0 + FA2_QK_GROUP; ++kb) {
-                    const half8 ka = *reinterpret_cast<const half8*>(ldsK + rdK[kk] + kb * 16 * D * 2);
+                    const half8 ka = *reinterpret_cast<const half8*>(ldsK + (rk ^ (kk << 6)) + kb * 16 * D * 2);
 #pragma unroll
                     for (int qb = 0; qb < QB; ++qb)
                         sacc[qb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qreg[qb][kk], sacc[qb][kb], 0, 0, 0);
@@ -593,7 +599,7 @@ void fa2_fwd_kernel(KernelArgs a) {
         auto pv_chunk = [&](int kc) __attribute__((always_inline)) {
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
-                const char* p0 = ldsV + rdV[db] + kc * 32 * D * 2;
+                const char* p0 = ldsV + (rv ^ (db << 5)) + kc * 32 * D * 2;
                 const s16x4 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p0);
                 const s16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0 + 16 * D * 2));
                 const half4 h0 = __builtin_bit_cast(half4, t0);
@@ -670,7 +676,15 @@ void fa2_fwd_kernel(KernelArgs a) {
             }
             if (ROWSUM_MFMA) {
                 // the tile's full row sums on the matrix unit (each lane gets
-                // its query's sum over all BN keys)
+                // its query's sum over all BN keys): an MFMA with an all-ones
+                // A operand sums the B operand (P^T) over its 32 keys. The
+                // constant is rebuilt here with volatile moves so that it is
+                // not kept live across the loop (it would be spilled).
+                uint32_t one2[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) asm volatile("v_mov_b32 %0, 0x3c003c00" : "=v"(one2[i]));
+                typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+                const half8 kOnes8 = __builtin_bit_cast(half8, u32x4v{one2[0], one2[1], one2[2], one2[3]});
 #pragma unroll
                 for (int qb = 0; qb < QB; ++qb) {
                     f32x4 ls = f32x4{0.f, 0.f, 0.f, 0.f};

@@ -14,7 +14,8 @@ library uses and checks, for many tensor shapes, that
     tile the kernel does not mask holds only admissible keys,
   * the dropout counter of each probability register names that register's key,
   * every LDS destination and LDS read stays inside the ring,
-  * the hoisted per-lane LDS read offsets equal the per-row formulas,
+  * the per-lane LDS read offsets (one base per tensor, XORed with the k-step
+    or column block) equal the per-row formulas,
   * the XOR swizzles put each ds_read_b128 quarter-wave (K) and each
     transposing-read half-wave (V) on distinct 16-byte bank groups of a
     256-byte window,
@@ -266,8 +267,14 @@ def test_lds_reads_and_bank_groups(D):
     TILE, DB, NKC, NKB, DK = BN * D, D // 16, BN // 32, BN // 16, D // 32
     lane = np.arange(64)
     l16, g = lane & 15, lane >> 4
+    # the kernel keeps one base per tensor and derives the k-step / column-block
+    # offsets by XOR; that must equal the per-row formula
+    rdK0 = 2 * (l16 * D + 8 * (g ^ swz_k(D, l16)))
+    r0v = 4 * g + (l16 >> 2)
+    rdV0 = 2 * (r0v * D + 8 * (((l16 & 3) >> 1) ^ swz_v(D, r0v)) + 4 * (l16 & 1))
     for kk in range(DK):
         hoisted = 2 * (l16 * D + 8 * ((4 * kk + g) ^ swz_k(D, l16)))
+        assert np.array_equal(rdK0 ^ (kk << 6), hoisted)
         for kb in range(NKB):
             r = 16 * kb + l16
             direct = 2 * (r * D + 8 * ((4 * kk + g) ^ swz_k(D, r)))
@@ -280,6 +287,7 @@ def test_lds_reads_and_bank_groups(D):
     for db in range(DB):
         lc = 2 * db + ((l16 & 3) >> 1)
         hoisted = 2 * (r0 * D + 8 * (lc ^ swz_v(D, r0)) + 4 * (l16 & 1))
+        assert np.array_equal(rdV0 ^ (db << 5), hoisted)
         for kc in range(NKC):
             for half in (0, 1):
                 r = 32 * kc + 16 * half + r0
