@@ -197,7 +197,7 @@ struct KernelArgs {
     int wl, wr;           // local window: keys i-wl .. i+wr (window kernels only)
     float c;              // scale * log2(e)
     float out_scale;      // 1/(1-p) with dropout, else 1
-    uint32_t drop_thr;    // a key is kept when its 32-bit draw is >= drop_thr
+    uint32_t drop_thr;    // a key is kept when its 16-bit draw is >= drop_thr
     uint32_t seed_lo, seed_hi, offset;
 };
 
@@ -565,26 +565,33 @@ void fa2_fwd_kernel(KernelArgs a) {
         };
 
         // ---- dropout on P: zero the probabilities of dropped keys ----
-        // Key j of query row i (both within the sequence) of head (b, h) draws
-        // word j%4 of Philox4x32-10 at counter (j/4, i, b*H + h, offset) under
-        // key (seed_lo, seed_hi), and is kept when that word is >= drop_thr. A
-        // lane's 4 keys of a 16-key block are 4 consecutive keys starting at a
-        // multiple of 4, i.e. one Philox call. Kept probabilities are scaled by
-        // 1/(1-p) in the epilogue.
+        // Key j of query row i (both within the sequence) of head (b, h) takes
+        // 16-bit draw j%8 of Philox4x32-10 at counter (j/8, i, b*H + h, offset)
+        // under key (seed_lo, seed_hi) (draw t = bits 16*(t%2) of word t/2),
+        // and is kept when the draw is >= drop_thr. A lane holds keys
+        // 4g..4g+3 of the two 16-key blocks of chunk kc; lanes g and g^1 (the
+        // two 16-lane rows a v_permlane16_swap pairs) need the same two groups
+        // of 8 keys, g even the low four draws and g odd the high four. So
+        // each lane computes one group (g even that of the first block, g odd
+        // that of the second) and two swaps hand each lane the other lane's
+        // words it needs. Kept probabilities are scaled by 1/(1-p) in the
+        // epilogue.
         auto drop_chunk = [&](int kc) __attribute__((always_inline)) {
+            const uint32_t group = (uint32_t)((k0 + 32 * kc) >> 3) + 2u * (uint32_t)(g & 1) + (uint32_t)(g >> 1);
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb) {
                 const uint32_t qrow = (uint32_t)(qw0 + 16 * qb + l16);
+                const U32x4 r = philox4x32_10(group, qrow, (uint32_t)bh, a.offset, a.seed_lo, a.seed_hi);
+                // after the swaps: x = this lane's two words for the first
+                // block, y = for the second
+                const auto s0 = __builtin_amdgcn_permlane16_swap(r.w[0], r.w[2], false, false);
+                const auto s1 = __builtin_amdgcn_permlane16_swap(r.w[1], r.w[3], false, false);
+                const uint32_t w[4] = {s0[0], s1[0], s0[1], s1[1]};
                 uint32_t m[4];
 #pragma unroll
-                for (int half_ = 0; half_ < 2; ++half_) {
-                    const uint32_t jg = (uint32_t)((k0 + 32 * kc + 16 * half_) >> 2) + (uint32_t)g;
-                    const U32x4 r = philox4x32_10(jg, qrow, (uint32_t)bh, a.offset, a.seed_lo, a.seed_hi);
-                    m[2 * half_ + 0] = (r.w[0] >= a.drop_thr ? 0x0000FFFFu : 0u) |
-                                       (r.w[1] >= a.drop_thr ? 0xFFFF0000u : 0u);
-                    m[2 * half_ + 1] = (r.w[2] >= a.drop_thr ? 0x0000FFFFu : 0u) |
-                                       (r.w[3] >= a.drop_thr ? 0xFFFF0000u : 0u);
-                }
+                for (int e = 0; e < 4; ++e)
+                    m[e] = ((w[e] & 0xFFFFu) >= a.drop_thr ? 0x0000FFFFu : 0u) |
+                           ((w[e] >> 16) >= a.drop_thr ? 0xFFFF0000u : 0u);
                 typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
                 u32x4v bits = __builtin_bit_cast(u32x4v, pb[qb][kc]);
                 bits &= u32x4v{m[0], m[1], m[2], m[3]};
@@ -947,8 +954,8 @@ TileShape dense_tile_shape(int D, long long units, int S, int window_left, int w
 
 uint32_t drop_threshold(float p) {
     if (!(p > 0.0f)) return 0u;
-    const double t = std::floor((double)p * 4294967296.0);
-    return t >= 4294967295.0 ? 0xFFFFFFFFu : (uint32_t)t;
+    const double t = std::floor((double)p * 65536.0);
+    return t >= 65535.0 ? 0xFFFFu : (uint32_t)t;
 }
 
 hipError_t launch_forward(const LaunchArgs& a, hipStream_t stream) {

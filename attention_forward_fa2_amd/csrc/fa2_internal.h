@@ -40,8 +40,8 @@ struct LaunchArgs {
     unsigned int offset;
 };
 
-// Keep threshold of a dropout probability: a key is kept when its 32-bit draw
-// is >= floor(p * 2^32) (clamped to 2^32 - 1).
+// Keep threshold of a dropout probability: a key is kept when its 16-bit draw
+// is >= floor(p * 2^16) (clamped to 2^16 - 1).
 uint32_t drop_threshold(float p);
 
 // Enqueues the kernel for already-validated arguments; returns the launch status.

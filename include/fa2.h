@@ -32,11 +32,14 @@
  *            O_i = sum_j P_ij z_ij v_j / (1 - p). LSE is that of the softmax
  *            before dropout. z_ij comes from Philox4x32-10 (Salmon et al.,
  *            SC 2011, "Parallel random numbers: as easy as 1, 2, 3"): with
- *            r = Philox4x32-10(counter = (j / 4, i, b*H + h, offset),
- *                              key = (seed mod 2^32, seed / 2^32)),
- *            z_ij = 1 when word j mod 4 of r is >= floor(p * 2^32) (clamped
- *            to 2^32 - 1), where i and j are row indices within the sequence
- *            and b is the batch index (the sequence index when packed).
+ *            r = Philox4x32-10(counter = (j / 8, i, b*H + h, offset),
+ *                              key = (seed mod 2^32, seed / 2^32))
+ *            read as eight 16-bit draws (draw t = bits 16*(t mod 2) .. +15 of
+ *            word t / 2), z_ij = 1 when draw j mod 8 is >= floor(p * 2^16)
+ *            (clamped to 2^16 - 1), where i and j are row indices within the
+ *            sequence and b is the batch index (the sequence index when
+ *            packed). The keep probability is therefore 1 - floor(p*2^16)/2^16,
+ *            within 2^-16 of 1 - p.
  *
  * Precision: fp16 inputs, fp32 accumulation (MFMA), fp32 softmax state, fp16
  * output rounded to nearest even, fp32 LSE.

@@ -142,10 +142,10 @@ def philox4x32_10(counter, key, lib=None):
 
 
 def dropout_threshold(p: float) -> int:
-    """floor(p * 2^32), clamped to 2^32 - 1: a draw >= it keeps the weight."""
+    """floor(p * 2^16), clamped to 2^16 - 1: a 16-bit draw >= it keeps the weight."""
     if not p > 0.0:
         return 0
-    return min(int(math.floor(float(p) * 4294967296.0)), 0xFFFFFFFF)
+    return min(int(math.floor(float(p) * 65536.0)), 0xFFFF)
 
 
 def _head(lib, q2, k2, v2, scale, window, dropout_p, seed, offset, bh, rows, nthreads):

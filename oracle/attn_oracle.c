@@ -47,11 +47,13 @@
  *     at a time and the Python wrapper does the selection.
  *   - dropout with probability p: after the softmax, P_ij is multiplied by
  *     z_ij / (1 - p) with z_ij in {0, 1}; l_i and LSE_i are those of the
- *     softmax before dropout. z_ij = 1 when word (j mod 4) of
- *     Philox4x32-10(counter = (floor(j/4), i, bh, offset), key = (k0, k1)) is
- *     >= thr, with thr = floor(p * 2^32) clamped to 2^32 - 1 and bh the
- *     flat (sequence, head) index. Philox4x32-10 follows Salmon, Moraes, Dror
- *     and Shaw, "Parallel random numbers: as easy as 1, 2, 3" (SC 2011).
+ *     softmax before dropout. The 128-bit output of
+ *     Philox4x32-10(counter = (floor(j/8), i, bh, offset), key = (k0, k1))
+ *     is read as eight 16-bit draws, draw t being bits 16*(t mod 2) .. +15
+ *     of word floor(t/2); z_ij = 1 when draw (j mod 8) is >= thr, with
+ *     thr = floor(p * 2^16) clamped to 2^16 - 1 and bh the flat (sequence,
+ *     head) index. Philox4x32-10 follows Salmon, Moraes, Dror and Shaw,
+ *     "Parallel random numbers: as easy as 1, 2, 3" (SC 2011).
  */
 #include <math.h>
 #include <stdint.h>
@@ -99,7 +101,7 @@ void attn_oracle_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uin
 
 struct dropout_cfg {
     int on;
-    uint32_t thr;        /* keep when the draw is >= thr */
+    uint32_t thr;        /* keep when the 16-bit draw is >= thr */
     uint32_t key[2];
     uint32_t offset;
     uint32_t bh;         /* flat (sequence, head) index */
@@ -109,10 +111,12 @@ struct dropout_cfg {
 /* z_ij of the dropout reading above. */
 static int kept(const struct dropout_cfg *dc, long long i, long long j)
 {
-    const uint32_t ctr[4] = {(uint32_t)(j / 4), (uint32_t)i, dc->bh, dc->offset};
+    const uint32_t ctr[4] = {(uint32_t)(j / 8), (uint32_t)i, dc->bh, dc->offset};
     uint32_t r[4];
     philox4x32_10(ctr, dc->key, r);
-    return r[j % 4] >= dc->thr;
+    const int t = (int)(j % 8);
+    const uint32_t draw = (r[t / 2] >> (16 * (t % 2))) & 0xFFFFu;
+    return draw >= dc->thr;
 }
 
 /* The admissible keys of query i, J_i = { lo .. hi }: 0 <= j < S and

@@ -298,22 +298,24 @@ def pin_varlen_is_per_sequence(lib):
 
 
 def _keep_mask(S, bh, seed, offset, thr, lib):
-    """z_ij from the generator: word j%4 of Philox(j//4, i, bh, offset) >= thr."""
+    """z_ij from the generator: 16-bit draw (j mod 8) of Philox(j // 8, i, bh,
+    offset), draw t being bits 16*(t % 2) of word t // 2, compared with thr."""
     z = np.zeros((S, S))
     for i in range(S):
-        for j4 in range((S + 3) // 4):
-            r = oracle.philox4x32_10([j4, i, bh, offset], [seed & 0xFFFFFFFF, seed >> 32], lib=lib)
-            for e in range(4):
-                if 4 * j4 + e < S:
-                    z[i, 4 * j4 + e] = 1.0 if r[e] >= thr else 0.0
+        for j8 in range((S + 7) // 8):
+            r = oracle.philox4x32_10([j8, i, bh, offset], [seed & 0xFFFFFFFF, seed >> 32], lib=lib)
+            for t in range(8):
+                if 8 * j8 + t < S:
+                    draw = (r[t // 2] >> (16 * (t % 2))) & 0xFFFF
+                    z[i, 8 * j8 + t] = 1.0 if draw >= thr else 0.0
     return z
 
 
 def pin_dropout_mask(lib):
     """Q = 0 and V = I (D = S): O_ij = P_ij z_ij / (1 - p) with P_ij = 1/n_i,
     so O exposes every keep decision z_ij, which must be the generator's, with
-    the counter (j // 4, i, b*H + h, offset) and the key from the seed. LSE is
-    that of the softmax before dropout."""
+    the counter (j // 8, i, b*H + h, offset), 16-bit draw j % 8 and the key
+    from the seed. LSE is that of the softmax before dropout."""
     B, H, S = 1, 2, 10
     q = np.zeros((B, H, S, S))
     k = _rand(111, (B, H, S, S))
@@ -353,10 +355,10 @@ def pin_dropout_statistics(lib):
     thr = oracle.dropout_threshold(p)
     for off in range(40):
         for i in range(8):
-            for j4 in range(6):
-                r = oracle.philox4x32_10([j4, i, 0, off], [99, 0], lib=lib)
-                kept += sum(1 for w in r if w >= thr)
-                n += 4
+            for j8 in range(3):
+                r = oracle.philox4x32_10([j8, i, 0, off], [99, 0], lib=lib)
+                kept += sum(1 for w in r for half in (w & 0xFFFF, w >> 16) if half >= thr)
+                n += 8
     sigma = math.sqrt(n * p * (1 - p))
     assert abs(kept - n * (1 - p)) < 6 * sigma, f"keep rate {kept / n:.4f} vs {1 - p}"
 

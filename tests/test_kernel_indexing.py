@@ -389,17 +389,40 @@ def test_malformed_sequence_tables_stay_in_bounds(D):
 
 def test_dropout_counter_names_the_register_key():
     """Element x of P^T register pb[qb][kc] of lane (l16, g) holds key
-    k0 + 32kc + 16(x//4) + 4g + x%4 (the S^T accumulator order). The kernel
-    draws it as word x%4 of the Philox call with first counter word
-    (k0 + 32kc + 16(x//4))/4 + g: the definition's (key // 4, word key % 4)."""
+    j = k0 + 32kc + 16(x//4) + 4g + x%4 (the S^T accumulator order). The
+    kernel computes one Philox group per lane, group(lane) = (k0 + 32kc)/8 +
+    2(g&1) + (g>>1), and after swapping words 0<->2 and 1<->3 with the partner
+    lane g^1 (v_permlane16_swap: rows 1 and 3 of the first operand trade with
+    rows 0 and 2 of the second) reads element x from word (2(x//4) + (x%4)//2)
+    of the swapped set, half x%2. That must be the definition's draw j%8 of
+    group j//8."""
     lane = np.arange(64)
     g = lane >> 4
+    partner = lane ^ 16
     for k0 in (0, 64, 4096 - 64, 123 * 64):
         for kc in range(2):
-            for x in range(8):
-                key = k0 + 32 * kc + 16 * (x // 4) + 4 * g + x % 4
-                half = x // 4
-                word = 2 * ((x % 4) // 2) + x % 2
-                jg = (k0 + 32 * kc + 16 * half) // 4 + g
-                assert np.array_equal(jg, key // 4) and word == x % 4
-                assert np.array_equal(key % 4, np.full(64, x % 4))
+            group = (k0 + 32 * kc) // 8 + 2 * (g & 1) + (g >> 1)
+            # symbolic words: (group, word index) held by each lane before the swaps
+            own = [[(int(group[l]), w) for w in range(4)] for l in range(64)]
+            odd_row = (g & 1) == 1
+            s0 = [None] * 64
+            s1 = [None] * 64
+            t0 = [None] * 64
+            t1 = [None] * 64
+            for l in range(64):
+                p = int(partner[l])
+                # permlane16_swap(a=w0, b=w2): result[0] = a on even rows, partner's b on odd rows;
+                # result[1] = partner's a on even rows, b on odd rows
+                s0[l] = own[l][0] if not odd_row[l] else own[p][2]
+                t0[l] = own[p][0] if not odd_row[l] else own[l][2]
+                s1[l] = own[l][1] if not odd_row[l] else own[p][3]
+                t1[l] = own[p][1] if not odd_row[l] else own[l][3]
+            for l in range(64):
+                w = [s0[l], s1[l], t0[l], t1[l]]
+                for x in range(8):
+                    key = k0 + 32 * kc + 16 * (x // 4) + 4 * int(g[l]) + x % 4
+                    grp, word = w[2 * (x // 4) + (x % 4) // 2]
+                    half = x % 2
+                    t = key % 8
+                    assert grp == key // 8, (k0, kc, l, x)
+                    assert (word, half) == (t // 2, t % 2), (k0, kc, l, x)

@@ -44,9 +44,12 @@ MUTANTS = {
                         "const long long base = (head / 2) * (long long)S * D;"),
     "dropout ignored": ("if (dc && dc->on)", "if (0)"),
     "dropout not rescaled": ("p[t] * dc->keep_scale : 0.0", "p[t] : 0.0"),
-    "dropout keeps the draws below the threshold": ("r[j % 4] >= dc->thr", "r[j % 4] < dc->thr"),
-    "dropout reads the wrong word": ("r[j % 4] >= dc->thr", "r[(j + 1) % 4] >= dc->thr"),
-    "dropout counter with query and key swapped": ("{(uint32_t)(j / 4), (uint32_t)i,", "{(uint32_t)(i / 4), (uint32_t)j,"),
+    "dropout keeps the draws below the threshold": ("return draw >= dc->thr;", "return draw < dc->thr;"),
+    "dropout reads the wrong word": ("r[t / 2] >> (16 * (t % 2))", "r[(t / 2 + 1) % 4] >> (16 * (t % 2))"),
+    "dropout reads the wrong half of a word": ("r[t / 2] >> (16 * (t % 2))", "r[t / 2] >> (16 * (1 - t % 2))"),
+    "dropout draws 32-bit": ("& 0xFFFFu;", "& 0xFFFFFFFFu;"),
+    "dropout counter with query and key swapped": ("{(uint32_t)(j / 8), (uint32_t)i,", "{(uint32_t)(i / 8), (uint32_t)j,"),
+    "dropout counter groups of four keys": ("{(uint32_t)(j / 8), (uint32_t)i,", "{(uint32_t)(j / 4), (uint32_t)i,"),
     "dropout counter without the head": ("(uint32_t)i, dc->bh, dc->offset}", "(uint32_t)i, 0u, dc->offset}"),
     "dropout counter without the offset": ("(uint32_t)i, dc->bh, dc->offset}", "(uint32_t)i, dc->bh, 0u}"),
     "dropout removes dropped weight from the normaliser": (

@@ -223,3 +223,30 @@ def test_reference_moves_in_some_workgroups_only(D):
         k[0, h, :, 0] = (np.arange(S) * 0.5).astype(np.float16)
     for causal in (False, True):
         full_case(q, k, v, causal, 1.0 / math.sqrt(D) if D == 64 else 0.125, f"mixed reference moves D={D}")
+
+
+@pytest.mark.parametrize("D,causal", [(64, False), (64, True), (128, True)])
+def test_long_sequence_sampled(D, causal):
+    """One very long sequence (S = 65536: 256 query tiles, 512 key tiles per
+    workgroup at full height): sampled rows against the oracle, including the
+    first and last rows and the last query tile."""
+    S = 65536
+    q, k, v = make_random(44_000 + D + int(causal), 1, 2, S, D)
+    O, L = gpu_forward(q, k, v, causal, 1.0 / math.sqrt(D))
+    g = np.random.Generator(np.random.PCG64(44_100 + D))
+    rows = np.unique(np.concatenate([[0, 1, S - 257, S - 1, S, 2 * S - 1], g.integers(0, 2 * S, size=40)]))
+    Oref, Lref = oracle.attention_rows(q, k, v, causal, float(np.float32(1.0 / math.sqrt(D))), rows)
+    check(O.reshape(-1, D)[rows], L.reshape(-1)[rows], Oref, Lref, f"S=65536 D={D} causal={causal}")
+
+
+def test_wide_grid_sampled():
+    """Many heads (B64 H32: 2048 heads, 4096 workgroups at D=64): one sampled
+    row per head, so every head's mapping is checked."""
+    B, H, S, D = 64, 32, 512, 64
+    q, k, v = make_random(45_000, B, H, S, D)
+    for causal in (False, True):
+        O, L = gpu_forward(q, k, v, causal, 0.125)
+        g = np.random.Generator(np.random.PCG64(45_001 + int(causal)))
+        rows = np.arange(B * H) * S + g.integers(0, S, size=B * H)
+        Oref, Lref = oracle.attention_rows(q, k, v, causal, 0.125, rows)
+        check(O.reshape(-1, D)[rows], L.reshape(-1)[rows], Oref, Lref, f"wide grid causal={causal}")
