@@ -283,6 +283,17 @@ __device__ __forceinline__ U32x4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_
 #ifndef FA2_SETPRIO
 #define FA2_SETPRIO 1
 #endif
+// Wave priorities (0..3) for the score MFMAs, the softmax that follows them and
+// the PV MFMAs; the priority returns to 0 after the PV block.
+#ifndef FA2_PRIO_QK
+#define FA2_PRIO_QK 2
+#endif
+#ifndef FA2_PRIO_SM
+#define FA2_PRIO_SM 0
+#endif
+#ifndef FA2_PRIO_PV
+#define FA2_PRIO_PV 1
+#endif
 // 16-key blocks whose score MFMAs are interleaved (1, 2 or 4; see compute_tile).
 #ifndef FA2_QK_GROUP
 #define FA2_QK_GROUP 4
@@ -460,7 +471,7 @@ void fa2_fwd_kernel(KernelArgs a) {
         asm volatile("" : "+v"(rk), "+v"(rv));
 
         // ---- S^T = K Q^T on MFMA ----
-        if (FA2_SETPRIO) __builtin_amdgcn_s_setprio(1);
+        if (FA2_SETPRIO) __builtin_amdgcn_s_setprio(FA2_PRIO_QK);
         f32x4 sacc[QB][NKB];
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
@@ -482,7 +493,7 @@ void fa2_fwd_kernel(KernelArgs a) {
                 }
             }
         }
-        if (FA2_SETPRIO) __builtin_amdgcn_s_setprio(0);
+        if (FA2_SETPRIO) __builtin_amdgcn_s_setprio(FA2_PRIO_SM);
 
         // ---- masks: keys past the end, after the query (causal), outside the
         // window (local) ----
@@ -722,7 +733,7 @@ void fa2_fwd_kernel(KernelArgs a) {
 #pragma unroll
             for (int kc = 0; kc < NKC; ++kc) drop_chunk(kc);
         }
-        if (FA2_SETPRIO) __builtin_amdgcn_s_setprio(1);
+        if (FA2_SETPRIO) __builtin_amdgcn_s_setprio(FA2_PRIO_PV);
 #pragma unroll
         for (int kc = 0; kc < NKC; ++kc) pv_chunk(kc);
         if (FA2_SETPRIO) __builtin_amdgcn_s_setprio(0);

@@ -250,3 +250,64 @@ def test_wide_grid_sampled():
         rows = np.arange(B * H) * S + g.integers(0, S, size=B * H)
         Oref, Lref = oracle.attention_rows(q, k, v, causal, 0.125, rows)
         check(O.reshape(-1, D)[rows], L.reshape(-1)[rows], Oref, Lref, f"wide grid causal={causal}")
+
+
+def test_hip_graph_replays():
+    """The forward pass captured in a HIP graph (torch.cuda.CUDAGraph) and
+    replayed three times on new inputs copied into the captured buffers, with
+    eager work and synchronisations between replays: every replay must equal
+    an eager launch on the same inputs bit for bit (the kernel writes every
+    output element and uses no memset)."""
+    import torch
+    import attention_forward_fa2_amd as fa2
+    dev = torch.device("cuda:0")
+    B, H, S, D = 2, 3, 333, 64
+    qs, ks, vs = (torch.empty((B, H, S, D), dtype=torch.float16, device=dev) for _ in range(3))
+    o = torch.empty_like(qs)
+    lse = torch.empty((B, H, S), dtype=torch.float32, device=dev)
+    q0, k0, v0 = make_random(46_000, B, H, S, D)
+    for t, x in zip((qs, ks, vs), (q0, k0, v0)):
+        t.copy_(torch.from_numpy(x))
+    fa2.forward(qs, ks, vs, causal=True, out=o, lse=lse)   # eager first: one-time device checks
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            fa2.forward(qs, ks, vs, causal=True, out=o, lse=lse)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        q, k, v = make_random(46_100 + 10 * rep, B, H, S, D)
+        for t, x in zip((qs, ks, vs), (q, k, v)):
+            t.copy_(torch.from_numpy(x))
+        o.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        O_g, L_g = o.cpu().numpy().copy(), lse.cpu().numpy().copy()
+        _ = (qs.float() * 2).sum().item()       # unrelated eager work between replays
+        O_e, L_e = gpu_forward(q, k, v, True, 1.0 / math.sqrt(D))
+        log(f"  graph replay {rep}: bitwise equal to eager = {np.array_equal(O_g.view(np.uint16), O_e.view(np.uint16))}")
+        assert np.array_equal(O_g.view(np.uint16), O_e.view(np.uint16))
+        assert np.array_equal(L_g.view(np.uint32), L_e.view(np.uint32))
+
+
+def test_concurrent_streams():
+    """Two launches on two streams at once, on different problems (D = 64
+    non-causal and D = 128 causal), each checked against the oracle."""
+    import torch
+    import attention_forward_fa2_amd as fa2
+    dev = torch.device("cuda:0")
+    cases = [(make_random(47_000, 2, 4, 700, 64), False, 64), (make_random(47_100, 1, 6, 900, 128), True, 128)]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = []
+    for (qkv, causal, D), st in zip(cases, streams):
+        tensors = [torch.from_numpy(x).to(dev) for x in qkv]
+        st.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(st):
+            outs.append(fa2.forward(*tensors, causal=causal, scale=1.0 / math.sqrt(D)) + tuple(tensors))
+    torch.cuda.synchronize()
+    for ((q, k, v), causal, D), (o, l, *_) in zip(cases, outs):
+        Oref, Lref = oracle.attention(q, k, v, causal, float(np.float32(1.0 / math.sqrt(D))))
+        check(o.cpu().numpy(), l.cpu().numpy(), Oref, Lref, f"stream D={D} causal={causal}")
