@@ -304,15 +304,6 @@ __device__ __forceinline__ U32x4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_
 #ifndef FA2_MFMA_ROWSUM
 #define FA2_MFMA_ROWSUM 2
 #endif
-// 1: run the softmax check and the PV product per 32-key chunk (see compute_tile).
-#ifndef FA2_KC_SPLIT
-#define FA2_KC_SPLIT 0
-#endif
-// With the split: VALU instructions to interleave after each PV MFMA (0 = leave
-// the order to the compiler).
-#ifndef FA2_KC_SCHED
-#define FA2_KC_SCHED 0
-#endif
 
 // Occupancy target of the dropout instances at D=64 (waves per SIMD); the
 // generator's registers do not fit the 4-wave budget without spills.
@@ -327,8 +318,7 @@ void fa2_fwd_kernel(KernelArgs a) {
     constexpr int D = SH::D, QB = SH::QB, NW = SH::NW, BN = SH::BN, QW = SH::QW, BM = SH::BM;
     constexpr int NKB = SH::NKB, NKC = SH::NKC, DK = SH::DK, DB = SH::DB, CPR = SH::CPR;
     constexpr int TILE = SH::TILE, LTILE = SH::LTILE, LOADS = SH::LOADS, SUB = SH::SUB, KB = SH::KB;
-    constexpr bool ROWSUM_MFMA =
-        !FA2_KC_SPLIT && (FA2_MFMA_ROWSUM == 1 || (FA2_MFMA_ROWSUM == 2 && (D == 128 || MASK == kNoMask)));
+    constexpr bool ROWSUM_MFMA = FA2_MFMA_ROWSUM == 1 || (FA2_MFMA_ROWSUM == 2 && (D == 128 || MASK == kNoMask));
 
     // LDS ring: [stage][K | V][LTILE] halves; a stage holds SUB compute tiles.
     extern __shared__ __attribute__((aligned(16))) _Float16 smem[];
@@ -629,61 +619,7 @@ void fa2_fwd_kernel(KernelArgs a) {
             }
         };
 
-#if FA2_KC_SPLIT
-        // Chunk by chunk: the check, and if needed the reference move, are done
-        // per 32-key chunk, so the PV product of chunk kc and the
-        // exponentials of chunk kc+1 share a basic block and can overlap in
-        // the wave's instruction stream. A reference move after chunk kc has
-        // been accumulated rescales it with the rest of o, as for any tile.
-        if (fresh) {
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb) move_reference(qb, row_max(qb, 0, NKB));
-        }
-#pragma unroll
-        for (int kc = 0; kc < NKC; ++kc) {
-            float rs[QB];
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb) {
-                rs[qb] = 0.f;
-                exp_chunk(qb, kc, rs[qb]);
-            }
-#if FA2_KC_SCHED
-            if (kc > 0) {
-                // This basic block also holds the PV product of chunk kc-1:
-                // alternate its MFMAs with the exponentials of chunk kc so the
-                // wave issues VALU work while the matrix unit is busy.
-                __builtin_amdgcn_sched_group_barrier(0x100, DB, 0);  // V reads of the first half
-#pragma unroll
-                for (int i = 0; i < DB * QB; ++i) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);          // one MFMA
-                    __builtin_amdgcn_sched_group_barrier(0x002, FA2_KC_SCHED, 0);  // VALU
-                    if (i == DB * QB / 2 - 1) __builtin_amdgcn_sched_group_barrier(0x100, DB, 0);
-                }
-            }
-#endif
-            if (!fresh) {
-                bool over = false;
-#pragma unroll
-                for (int qb = 0; qb < QB; ++qb) over |= !(rs[qb] < kSpeculateLimit);
-                if (__builtin_amdgcn_ballot_w64(over) != 0) {  // wave-uniform
-#pragma unroll
-                    for (int qb = 0; qb < QB; ++qb) {
-                        move_reference(qb, row_max(qb, 2 * kc, 2 * kc + 2));
-                        rs[qb] = 0.f;
-                        exp_chunk(qb, kc, rs[qb]);
-                    }
-                }
-            }
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb) l_run[qb] += rs[qb];
-            if (DROP) drop_chunk(kc);
-            if (FA2_SETPRIO) __builtin_amdgcn_s_setprio(1);
-            pv_chunk(kc);
-            if (FA2_SETPRIO) __builtin_amdgcn_s_setprio(0);
-        }
-        fresh = false;
-#else
-        // Whole tile at once: exponentiate every chunk, one check per tile.
+        // Exponentiate the whole tile, then one check per tile.
         float rs[QB];
         auto exponentiate = [&]() __attribute__((always_inline)) {
 #pragma unroll
@@ -737,7 +673,6 @@ void fa2_fwd_kernel(KernelArgs a) {
 #pragma unroll
         for (int kc = 0; kc < NKC; ++kc) pv_chunk(kc);
         if (FA2_SETPRIO) __builtin_amdgcn_s_setprio(0);
-#endif
     };
 
     // One step of the scan over ring stage t (SUB compute tiles) held in stage ST.
