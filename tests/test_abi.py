@@ -215,6 +215,21 @@ def test_kernel_config():
         fa2.fa2_kernel_config(1, 1, 128, 80, 0)
 
 
+def test_kernel_config_shapes():
+    """Causal grids that fit in one round of resident workgroups (2 per CU at
+    D=64, 1 at D=128, 256 CUs) use half-height workgroups; others, and every
+    non-causal grid, the full height."""
+    full64 = fa2.fa2_kernel_config(4, 8, 4096, 64, 0)
+    assert (full64["rows_per_block"], full64["threads_per_block"], full64["blocks"]) == (256, 512, 512)
+    half64 = fa2.fa2_kernel_config(4, 8, 4096, 64, 1)      # 512 full-height blocks: one round
+    assert (half64["rows_per_block"], half64["threads_per_block"], half64["blocks"]) == (128, 256, 1024)
+    assert half64["lds_bytes"] < full64["lds_bytes"]
+    assert fa2.fa2_kernel_config(4, 8, 4100, 64, 1)["rows_per_block"] == 256   # 544 blocks: more than one round
+    assert fa2.fa2_kernel_config(1, 32, 16384, 64, 1)["rows_per_block"] == 256
+    assert fa2.fa2_kernel_config(1, 16, 4096, 128, 1)["rows_per_block"] == 128  # 256 blocks, 1 per CU
+    assert fa2.fa2_kernel_config(2, 16, 8192, 128, 1)["rows_per_block"] == 256
+
+
 def test_forward_rejects_bad_tensors():
     import torch
     q = torch.zeros((1, 1, 8, 64), dtype=torch.float16)
