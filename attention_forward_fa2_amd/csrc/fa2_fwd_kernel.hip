@@ -8,7 +8,8 @@
 // Every wave owns its query rows from the scores to the output, so waves never
 // combine partial results (the Q split of §"TiledMMA：把四个 warp 只铺在 M 维").
 //
-// gfx950 mapping (lane layouts measured on the device, see the design notes):
+// gfx950 mapping (lane layouts measured on the device with a probe that sends
+// integer matrices through the instructions and compares with a CPU product):
 //   * MFMA v_mfma_f32_16x16x32_f16. For a 16x32 A, 32x16 B and 16x16 C:
 //       A[i][k] -> lane i + 16*(k/8), element k%8
 //       B[k][j] -> lane j + 16*(k/8), element k%8
@@ -26,9 +27,12 @@
 //     V tile with the transposing LDS read ds_read_b64_tr_b16, which gives lane i
 //     of a 16-lane group 4 consecutive rows of column i (§"V 的转置只发生在视图里":
 //     V is never transposed in memory).
-//   * The row max and the final row sum combine the 4 lanes that share a query
-//     (lanes l, l^16, l^32, l^48) with v_permlane16_swap / v_permlane32_swap:
-//     the reduction group follows the accumulator ownership (§"把 lane 公式真正写出来").
+//   * The row max combines the 4 lanes that share a query (lanes l, l^16,
+//     l^32, l^48) with v_permlane16_swap / v_permlane32_swap: the reduction
+//     group follows the accumulator ownership (§"把 lane 公式真正写出来"). The
+//     row sum is either kept per lane (v_dot2 on the fp16 P) and combined the
+//     same way at the end, or taken on the matrix unit by an MFMA with an
+//     all-ones A operand, which hands every lane its query's full sum.
 //   * K and V tiles go HBM -> LDS with 16-byte direct-to-LDS loads
 //     (global_load_lds_dwordx4, LDS destination = base + 16*lane) into a
 //     two-stage ring (§"多 Stage 流水"); the tile for step t+1 is in flight while
@@ -37,6 +41,14 @@
 //   * Softmax runs in base 2: the max is taken on raw scores, then
 //     p = 2^(s*c - m*c) with c = scale*log2(e), one FMA and one v_exp_f32 per
 //     score (§"沿 C fragment 做 Online Softmax", closing paragraph).
+//
+// The same kernel serves the features §"哪些结论可以迁移，哪些只是本例特例" lists
+// for a production FA2: query heads sharing K/V heads (GQA/MQA: the K/V head
+// index in the base address), local windows (a mask kind that bounds the ring
+// stages a workgroup loads and the tiles each wave computes), packed sequences
+// of different lengths (tensors addressed through strides, sequence start and
+// length read from a table), and dropout on P (a counter-based generator,
+// Philox4x32-10, evaluated in registers).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -62,8 +74,9 @@ constexpr double kLog2e = 1.44269504088896340736;
 // Finite start value of the running max: exp2((m0 - m) * c) is exactly 0 for any
 // real score m, and a row whose keys were all masked so far keeps alpha = 1, p = 0.
 constexpr float kMaxInit = -1.0e30f;
-// A lane's partial row sum of fp16 probabilities below this bound means none of
-// them overflowed fp16 (largest finite 65504).
+// A row sum of fp16 probabilities (a lane's partial sum, or the tile's full
+// sum) below this bound means none of them overflowed fp16 (largest finite
+// 65504).
 constexpr float kSpeculateLimit = 32768.0f;
 
 template <int D_, int QB_, int NW_, int BN_, int SUB_>

@@ -43,10 +43,17 @@ def log(msg):
 
 
 def kernel_source_hash() -> str:
+    """sha256 of the kernel sources with comments and blank space removed, so
+    that only a change of code (not of a comment) voids the counter record."""
+    import re
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
-        with open(p, "rb") as f:
-            h.update(f.read())
+        with open(p, encoding="utf-8") as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        text = re.sub(r"\s+", " ", text).strip()
+        h.update(text.encode("utf-8"))
     return h.hexdigest()
 
 
