@@ -174,6 +174,39 @@ def feature_setup(key: str, causal: bool, dev):
     return f, step, 4.0 * f.D * pairs, cfg, cpu
 
 
+def gemm_calibration(reps: int) -> None:
+    """Median rate of plain fp16/bf16 matrix products through torch (hipBLASLt), one
+    JSON line each: what a vendor GEMM sustains on this GPU, the practical
+    MFMA ceiling beside the 2516.6 TFLOP/s dense fp16 peak. The last two are the
+    attention-shaped products of the unfused path (S = Q K^T, then P V) at
+    B*H = 32, S = 4096, D = 64."""
+    import torch
+    dev = torch.device("cuda:0")
+    cases = [(dt, (m, n, k), 1) for dt in (torch.float16, torch.bfloat16)
+             for (m, n, k) in ((4096, 4096, 4096), (8192, 8192, 8192), (16384, 16384, 8192))]
+    cases += [(torch.float16, (4096, 4096, 64), 32), (torch.float16, (4096, 64, 4096), 32)]
+    for dt, (m, n, k), batch in cases:
+        g = torch.Generator(device=dev).manual_seed(7)
+        a = torch.randn(batch, m, k, device=dev, dtype=dt, generator=g)
+        b = torch.randn(batch, k, n, device=dev, dtype=dt, generator=g)
+        fn = (lambda: torch.matmul(a[0], b[0])) if batch == 1 else (lambda: torch.bmm(a, b))
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for e0, e1 in ev:
+            e0.record()
+            fn()
+            e1.record()
+        torch.cuda.synchronize()
+        ms = sorted(e0.elapsed_time(e1) for e0, e1 in ev)[reps // 2]
+        tf = 2.0 * batch * m * n * k / (ms * 1e-3) / 1e12
+        print(json.dumps({"gemm": f"{batch}x{m}x{n}x{k}", "dtype": str(dt).replace("torch.", ""),
+                          "median_us": round(ms * 1e3, 1), "tflops": round(tf, 1),
+                          "frac_of_2516.6": round(tf / 2516.6, 3)}), flush=True)
+        del a, b
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -191,7 +224,14 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the benchmark, run 10 plain device-to-device copies of MIB MiB "
                          "(the reference kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
+    ap.add_argument("--gemm-calibration", action="store_true",
+                    help="instead of the benchmark, time plain fp16/bf16 matrix products through torch "
+                         "(hipBLASLt): the MFMA rate a vendor GEMM sustains on this GPU")
     args = ap.parse_args()
+
+    if args.gemm_calibration:
+        gemm_calibration(max(args.steps, 5))
+        return
 
     if args.copy_calibration:
         import torch
