@@ -212,6 +212,7 @@ struct KernelArgs {
     float out_scale;      // 1/(1-p) with dropout, else 1
     uint32_t drop_thr;    // a key is kept when its 16-bit draw is >= drop_thr
     uint32_t seed_lo, seed_hi, offset;
+    int serp;             // one-round causal grids: workgroups per serpentine band (CUs per XCD), else 0
 };
 
 enum MaskKind { kNoMask = 0, kCausal = 1, kWindow = 2 };
@@ -225,7 +226,13 @@ enum MaskKind { kNoMask = 0, kCausal = 1, kWindow = 2 };
 //  * causal with (sequences * K/V heads) a multiple of 8: XCD x gets K/V heads
 //    x, x+8, ... with all query heads of each, and walks them heaviest query
 //    tile first (the last tiles see the most keys), so the long workgroups
-//    start early and each K/V head has several tiles in flight on one XCD;
+//    start early and each K/V head has several tiles in flight on one XCD.
+//    When the whole grid is resident at once (one round, nothing refills a
+//    compute unit), the walk is a serpentine instead: bands of a.serp
+//    consecutive workgroups of an XCD (one per compute unit of the XCD) run
+//    alternately heaviest-first and lightest-first, so that the workgroups a
+//    compute unit receives, one from each band, add up to the same number of
+//    keys on every compute unit;
 //  * causal otherwise: heaviest tiles first over all heads;
 //  * packed sequences of different lengths: (sequence, K/V head) unit u goes
 //    to XCD u mod 8, so that with 8 or more heads every XCD gets its share of
@@ -248,8 +255,13 @@ __device__ __forceinline__ bool map_block(const KernelArgs& a, int bid, int& bh,
     }
     if (MASK == kCausal && (a.BHkv & 7) == 0) {
         const int per_tile = (a.BHkv >> 3) * a.group;  // query heads per XCD
-        qt = a.nqt - 1 - slot / per_tile;
-        const int r = slot % per_tile;
+        int s = slot;
+        if (a.serp) {
+            const int band = s / a.serp;  // complete odd bands run backwards
+            if ((band & 1) && (band + 1) * a.serp <= (a.nblocks >> 3)) s = band * a.serp + (a.serp - 1 - s % a.serp);
+        }
+        qt = a.nqt - 1 - s / per_tile;
+        const int r = s % per_tile;
         bh = (xcd + 8 * (r / a.group)) * a.group + r % a.group;
         return true;
     }
@@ -865,6 +877,8 @@ hipError_t launch_d(const LaunchArgs& a, hipStream_t stream) {
     k.nqt = (a.S + SH::BM - 1) / SH::BM;
     k.nblocks = a.cu_seqlens ? ((k.BHkv + 7) / 8) * 8 * k.nqt * k.group : k.BH * k.nqt;
     k.c = (float)((double)a.scale * kLog2e);
+    // A dense grid that is resident in one round takes the serpentine causal order.
+    k.serp = (!a.cu_seqlens && k.nblocks <= kCUs * wg_per_cu<SH>()) ? kCUs / 8 : 0;
 
     // Window: a negative or out-of-range side is unbounded (S keys).
     const bool left_open = a.window_left < 0 || a.window_left >= a.S;

@@ -71,15 +71,22 @@ def test_packed_mapping(BHkv, group, nqt, causal):
     assert np.array_equal(xcd, (bh // group) % 8)
 
 
-def block_map(BH, nqt, causal, group=1):
+def block_map(BH, nqt, causal, group=1, serp=0):
+    """serp: workgroups per serpentine band (the host passes the CUs per XCD
+    when the grid is resident in one round), 0 for the heaviest-first walk."""
     nb = BH * nqt
     bid = np.arange(nb)
     xcd, slot = bid & 7, bid >> 3
     BHkv = BH // group
     if causal and BHkv % 8 == 0:
         per_tile = (BHkv >> 3) * group
-        r = slot % per_tile
-        return (xcd + 8 * (r // group)) * group + r % group, nqt - 1 - slot // per_tile
+        s = slot.copy()
+        if serp:
+            band = s // serp
+            back = ((band & 1) == 1) & ((band + 1) * serp <= (nb >> 3))
+            s = np.where(back, band * serp + (serp - 1 - s % serp), s)
+        r = s % per_tile
+        return (xcd + 8 * (r // group)) * group + r % group, nqt - 1 - s // per_tile
     per, rem = nb >> 3, nb & 7
     logical = xcd * per + np.minimum(xcd, rem) + slot
     if causal:
@@ -94,6 +101,33 @@ def test_block_mapping_is_a_bijection(BH, nqt, causal):
     bh, qt = block_map(BH, nqt, causal)
     assert bh.min() >= 0 and bh.max() < BH and qt.min() >= 0 and qt.max() < nqt
     assert len(set(zip(bh.tolist(), qt.tolist()))) == BH * nqt
+
+
+@pytest.mark.parametrize("BHkv,group", [(8, 1), (16, 1), (32, 1), (64, 1), (8, 4), (24, 2)])
+@pytest.mark.parametrize("nqt", [1, 5, 8, 16, 32, 33, 64])
+def test_serpentine_causal_mapping(BHkv, group, nqt):
+    """One-round causal grids: with 32 workgroups per band the walk is still a
+    bijection, keeps each K/V head on one XCD, and when slot s of an XCD lands
+    on compute unit s mod 32 every compute unit of an XCD receives the same
+    number of key tiles to scan, up to one band's spread (the last, partial
+    band is not reversed)."""
+    BH = BHkv * group
+    bh, qt = block_map(BH, nqt, True, group, serp=32)
+    assert bh.min() >= 0 and bh.max() < BH and qt.min() >= 0 and qt.max() < nqt
+    assert len(set(zip(bh.tolist(), qt.tolist()))) == BH * nqt
+    xcd = np.arange(BH * nqt) & 7
+    kv = bh // group
+    for h in range(BHkv):
+        assert len(set(xcd[kv == h].tolist())) == 1
+    slots = BH * nqt // 8
+    if slots % 64 == 0:  # whole pairs of bands: every compute unit gets the same load
+        for x in range(8):
+            work = (qt + 1)[xcd == x]          # key tiles scanned, in slot order
+            load = np.bincount(np.arange(slots) % 32, weights=work, minlength=32)
+            assert load.max() == load.min()
+    plain_bh, plain_qt = block_map(BH, nqt, True, group)
+    if slots <= 32:  # a single band is never reversed
+        assert np.array_equal(bh, plain_bh) and np.array_equal(qt, plain_qt)
 
 
 @pytest.mark.parametrize("BHkv,group", [(8, 2), (8, 4), (16, 3), (24, 8), (32, 1), (4, 4), (12, 2), (1, 32)])
