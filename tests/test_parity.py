@@ -252,6 +252,27 @@ def test_wide_grid_sampled():
         check(O.reshape(-1, D)[rows], L.reshape(-1)[rows], Oref, Lref, f"wide grid causal={causal}")
 
 
+@pytest.mark.parametrize("D,B,H", [(64, 4, 8), (128, 1, 16)])
+def test_one_round_causal_every_workgroup(D, B, H):
+    """Causal grids resident in one round (half-height workgroups, serpentine
+    order with reversed bands): one sampled row in every workgroup's 128-row
+    block of every head against the oracle, so every workgroup of the
+    permuted order is checked."""
+    import attention_forward_fa2_amd as fa2
+    S = 4096
+    cfg = fa2.fa2_kernel_config(B, H, S, D, 1)
+    assert cfg["rows_per_block"] == 128 and cfg["blocks"] == B * H * S // 128
+    log(f"case one-round causal D={D} B={B} H={H} S={S}: {cfg}")
+    q, k, v = make_random(46_000 + D, B, H, S, D)
+    scale = 1.0 / math.sqrt(D)
+    O, L = gpu_forward(q, k, v, True, scale)
+    g = np.random.Generator(np.random.PCG64(46_100 + D))
+    blocks = np.arange(B * H * S // 128)
+    rows = blocks * 128 + g.integers(0, 128, size=blocks.size)
+    Oref, Lref = oracle.attention_rows(q, k, v, True, float(np.float32(scale)), rows)
+    check(O.reshape(-1, D)[rows], L.reshape(-1)[rows], Oref, Lref, f"one-round causal D={D}")
+
+
 def test_hip_graph_replays():
     """The forward pass captured in a HIP graph (torch.cuda.CUDAGraph) and
     replayed three times on new inputs copied into the captured buffers, with
