@@ -71,8 +71,9 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr double kLog2e = 1.44269504088896340736;
-// Finite start value of the running max: exp2((m0 - m) * c) is exactly 0 for any
-// real score m, and a row whose keys were all masked so far keeps alpha = 1, p = 0.
+// Finite start value of the running reference (base-2 units, i.e. a score times
+// c): exp2(m0 - m*c) is exactly 0 for any real score m, and a row whose keys
+// were all masked so far keeps alpha = 1, p = 0.
 constexpr float kMaxInit = -1.0e30f;
 // A row sum of fp16 probabilities (a lane's partial sum, or the tile's full
 // sum) below this bound means none of them overflowed fp16 (largest finite
@@ -453,10 +454,13 @@ void fa2_fwd_kernel(KernelArgs a) {
     for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) oacc[db][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m_run[QB], l_run[QB];
+    // Per query row: the running reference in base-2 units (a score times c,
+    // kept scaled so that the exponent needs one FMA and no multiply) and the
+    // running sum l.
+    float mc_run[QB], l_run[QB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-        m_run[qb] = kMaxInit;
+        mc_run[qb] = kMaxInit;
         l_run[qb] = 0.f;
     }
     const half2 kOnes2 = half2{(_Float16)1.0f, (_Float16)1.0f};
@@ -533,9 +537,10 @@ void fa2_fwd_kernel(KernelArgs a) {
         }
 
         // ---- online softmax update ----
-        // Probabilities are taken against the running reference m_run:
-        // p = 2^(s*c - m_run*c). l and o always use the same reference per row,
-        // so O = o/l and LSE = scale*m_run + ln l hold for any reference; the
+        // Probabilities are taken against the running reference m (held as
+        // mc_run = m*c): p = 2^(s*c - m*c). l and o always use the same
+        // reference per row, so O = o/l and LSE = scale*m + ln l hold for any
+        // reference; the
         // reference only has to keep every p representable in fp16. The
         // common path therefore skips the row max: it exponentiates against
         // the current reference and accepts the result if the row sum of the
@@ -543,7 +548,7 @@ void fa2_fwd_kernel(KernelArgs a) {
         // tile's full row sum) stays below 2^15, so no p overflowed. The
         // first tile, or a chunk that fails the check, takes the row max
         // (combined over the 4 lanes of a query), moves the reference to
-        // max(m_run, max), rescales o and l by alpha = 2^((m_old - m_new)*c)
+        // max(m, max), rescales o and l by alpha = 2^((m_old - m_new)*c)
         // and exponentiates again: the update of the online softmax.
         half8 pb[QB][NKC];
 
@@ -552,7 +557,7 @@ void fa2_fwd_kernel(KernelArgs a) {
         // the fp16 values, before dropout: the softmax normaliser counts every
         // admissible key).
         auto exp_chunk = [&](int qb, int kc, float& rsum) __attribute__((always_inline)) {
-            const float mc = m_run[qb] * a.c;
+            const float mc = mc_run[qb];
             const f32x4 lo = sacc[qb][2 * kc], hi = sacc[qb][2 * kc + 1];
             half2 h[4];
 #pragma unroll
@@ -580,11 +585,13 @@ void fa2_fwd_kernel(KernelArgs a) {
             }
             return max_xor32(max_xor16(fmaxf(a0, a1)));
         };
-        // Move the reference of query block qb up to mx (if higher), rescaling o and l.
+        // Move the reference of query block qb up to the raw score mx (if
+        // higher), rescaling o and l. Rounding is monotonic, so max(m*c, mx*c)
+        // is the scaled maximum exactly.
         auto move_reference = [&](int qb, float mx) __attribute__((always_inline)) {
-            const float m_new = fmaxf(m_run[qb], mx);
-            const float alpha = __builtin_amdgcn_exp2f((m_run[qb] - m_new) * a.c);
-            m_run[qb] = m_new;
+            const float m_new = fmaxf(mc_run[qb], mx * a.c);
+            const float alpha = __builtin_amdgcn_exp2f(mc_run[qb] - m_new);
+            mc_run[qb] = m_new;
             l_run[qb] *= alpha;
 #pragma unroll
             for (int db = 0; db < DB; ++db) oacc[db][qb] *= alpha;
@@ -749,7 +756,7 @@ void fa2_fwd_kernel(KernelArgs a) {
                                        (_Float16)(ov[2] * inv), (_Float16)(ov[3] * inv)};
                 *reinterpret_cast<half4*>(Oh + (long long)row * q_sr + 16 * db + 4 * g) = hv;
             }
-            if (g == 0) Lh[row] = (m_run[qb] * a.c + log2f(lt)) * kLn2;
+            if (g == 0) Lh[row] = (mc_run[qb] + log2f(lt)) * kLn2;
         }
     }
 }
