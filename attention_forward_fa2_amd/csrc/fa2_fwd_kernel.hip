@@ -214,6 +214,7 @@ struct KernelArgs {
     uint32_t drop_thr;    // a key is kept when its 16-bit draw is >= drop_thr
     uint32_t seed_lo, seed_hi, offset;
     int serp;             // one-round causal grids: workgroups per serpentine band (CUs per XCD), else 0
+    int lpt;              // packed launches: walk the sequences longest first (at most 64 sequences)
 };
 
 enum MaskKind { kNoMask = 0, kCausal = 1, kWindow = 2 };
@@ -239,20 +240,50 @@ enum MaskKind { kNoMask = 0, kCausal = 1, kWindow = 2 };
 //    to XCD u mod 8, so that with 8 or more heads every XCD gets its share of
 //    every sequence whatever the lengths; an XCD walks its units one by one
 //    (all query tiles of a unit and all query heads of its group together;
-//    causal: heaviest tile first). The grid then has ceil(units/8)*8*nqt*group
-//    workgroups, and those past the last unit, or past the end of a short
-//    sequence, exit at once. Returns false for a workgroup with no work.
+//    causal: heaviest tile first). With at most 64 sequences the units are
+//    numbered longest sequence first (each workgroup ranks the lengths from
+//    the table itself), so that the long workgroups start early and short
+//    ones fill the end of the launch. The grid then has
+//    ceil(units/8)*8*nqt*group workgroups, and those past the last unit, or
+//    past the end of a short sequence, exit at once. Returns false for a
+//    workgroup with no work.
+// Index of the sequence that ranks rho-th by length, longest first (ties by
+// index), among nseq <= 64 sequences of a packed table: lane j takes sequence
+// j's clamped length, counts the sequences that rank before it, and the lane
+// whose count is rho names the sequence. Every wave computes the same answer.
+__device__ __forceinline__ int sequence_of_rank(const KernelArgs& a, int nseq, int rho) {
+    const int lane = threadIdx.x & 63;
+    int len = -1;
+    if (lane < nseq) {
+        const int s0 = min(max(a.cu[lane], 0), a.total);
+        const int s1 = min(max(a.cu[lane + 1], s0), a.total);
+        len = min(s1 - s0, a.S);
+    }
+    int rank = 0;
+    for (int i = 0; i < nseq; ++i) {
+        const int li = __builtin_amdgcn_readlane(len, i);
+        rank += (li > len) || (li == len && i < lane);
+    }
+    const unsigned long long hit = __builtin_amdgcn_ballot_w64(lane < nseq && rank == rho);
+    return hit ? __builtin_ctzll(hit) : 0;
+}
+
 template <int MASK>
 __device__ __forceinline__ bool map_block(const KernelArgs& a, int bid, int& bh, int& qt) {
     const int xcd = bid & 7, slot = bid >> 3;
     if (a.cu) {
         const int per_unit = a.nqt * a.group;
-        const int kvu = xcd + 8 * (slot / per_unit);
+        int kvu = xcd + 8 * (slot / per_unit);
         const int rem = slot % per_unit;
+        if (kvu >= a.BHkv) return false;
+        if (a.lpt) {
+            const int H_kv = a.H / a.group;
+            kvu = sequence_of_rank(a, a.BHkv / H_kv, kvu / H_kv) * H_kv + kvu % H_kv;
+        }
         qt = rem / a.group;
         if (MASK == kCausal) qt = a.nqt - 1 - qt;
         bh = kvu * a.group + rem % a.group;
-        return kvu < a.BHkv;
+        return true;
     }
     if (MASK == kCausal && (a.BHkv & 7) == 0) {
         const int per_tile = (a.BHkv >> 3) * a.group;  // query heads per XCD
@@ -886,6 +917,8 @@ hipError_t launch_d(const LaunchArgs& a, hipStream_t stream) {
     k.c = (float)((double)a.scale * kLog2e);
     // A dense grid that is resident in one round takes the serpentine causal order.
     k.serp = (!a.cu_seqlens && k.nblocks <= kCUs * wg_per_cu<SH>()) ? kCUs / 8 : 0;
+    // Packed tables of up to 64 sequences (one per lane) are walked longest first.
+    k.lpt = (a.cu_seqlens && a.B <= 64) ? 1 : 0;
 
     // Window: a negative or out-of-range side is unbounded (S keys).
     const bool left_open = a.window_left < 0 || a.window_left >= a.S;

@@ -39,9 +39,20 @@ SHAPES = {64: (2, 8, 64, 2), 128: (2, 8, 64, 2)}
 VARIANTS = [(2, 8, 64, 1), (2, 8, 64, 2), (2, 4, 64, 1), (2, 4, 64, 2), (4, 4, 64, 1)]
 
 
-def block_map_packed(BH, nqt, causal, group=1):
+def sequence_of_rank(lens, rho):
+    """The kernel's ranking: the sequence whose count of sequences ranking
+    before it (longer, or as long with a lower index) is rho."""
+    n = len(lens)
+    ranks = [sum((lens[i] > lens[j]) or (lens[i] == lens[j] and i < j) for i in range(n)) for j in range(n)]
+    hits = [j for j in range(n) if ranks[j] == rho]
+    assert len(hits) == 1
+    return hits[0]
+
+
+def block_map_packed(BH, nqt, causal, group=1, lens=None):
     """Packed sequences: (sequence, K/V head) unit u on XCD u mod 8, unit by
-    unit. Returns (bh, qt, valid) over the padded grid."""
+    unit; with lens given (at most 64 sequences) the units are numbered
+    longest sequence first. Returns (bh, qt, valid) over the padded grid."""
     BHkv = BH // group
     nb = -(-BHkv // 8) * 8 * nqt * group
     bid = np.arange(nb)
@@ -49,10 +60,15 @@ def block_map_packed(BH, nqt, causal, group=1):
     per_unit = nqt * group
     kvu = xcd + 8 * (slot // per_unit)
     rem = slot % per_unit
+    valid = kvu < BHkv
+    if lens is not None:
+        H_kv = BHkv // len(lens)
+        order = [sequence_of_rank(lens, r) for r in range(len(lens))]
+        kvu = np.where(valid, np.array(order + [0])[np.minimum(kvu // H_kv, len(lens))] * H_kv + kvu % H_kv, kvu)
     qt = rem // group
     if causal:
         qt = nqt - 1 - qt
-    return kvu * group + rem % group, qt, kvu < BHkv
+    return kvu * group + rem % group, qt, valid
 
 
 @pytest.mark.parametrize("BHkv", [1, 3, 8, 12, 24, 40])
@@ -69,6 +85,28 @@ def test_packed_mapping(BHkv, group, nqt, causal):
     assert len(set(zip(bh.tolist(), qt.tolist()))) == BH * nqt == ok.sum()
     xcd = np.nonzero(ok)[0] & 7
     assert np.array_equal(xcd, (bh // group) % 8)
+
+
+@pytest.mark.parametrize("nseq", [1, 2, 7, 24, 64])
+@pytest.mark.parametrize("H_kv,group", [(1, 1), (2, 4), (8, 1)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_packed_mapping_longest_first(nseq, H_kv, group, causal):
+    """Longest-first packed order: still every (unit, query tile) exactly once
+    among the valid workgroups and each K/V unit on one XCD; along the unit
+    numbering the sequence lengths never increase; ties and empty sequences
+    (a malformed table clamps to such lengths) keep it a bijection."""
+    g = np.random.Generator(np.random.PCG64(nseq * 31 + H_kv))
+    lens = [int(x) if g.random() > 0.2 else int(g.choice([0, 5])) for x in g.integers(0, 3000, size=nseq)]
+    BH, nqt = nseq * H_kv * group, 3
+    bh, qt, ok = block_map_packed(BH, nqt, causal, group, lens)
+    bh, qt = bh[ok], qt[ok]
+    assert len(set(zip(bh.tolist(), qt.tolist()))) == BH * nqt == ok.sum()
+    kv = bh // group
+    xcd = np.nonzero(ok)[0] & 7
+    for u in range(nseq * H_kv):
+        assert len(set(xcd[kv == u].tolist())) == 1
+    order = [sequence_of_rank(lens, r) for r in range(nseq)]
+    assert [lens[b] for b in order] == sorted(lens, reverse=True)
 
 
 def block_map(BH, nqt, causal, group=1, serp=0):
@@ -180,7 +218,12 @@ def emulate(B, H, S, D, causal, shape=None, H_kv=None, cu=None, total=None, wind
     if cu is None:
         bhs, qts = block_map(B * H, nqt, mode == "causal", group)
     else:
-        bhs, qts, valid = block_map_packed(B * H, nqt, mode == "causal", group)
+        # the kernel's clamped lengths, ranked longest first for up to 64 sequences
+        lens = []
+        for i in range(B):
+            s0 = min(max(int(cu[i]), 0), total)
+            lens.append(min(min(max(int(cu[i + 1]), s0), total) - s0, S))
+        bhs, qts, valid = block_map_packed(B * H, nqt, mode == "causal", group, lens if B <= 64 else None)
         bhs, qts = bhs[valid], qts[valid]
         assert len(set(zip(bhs.tolist(), qts.tolist()))) == B * H * nqt
     for bh, qt in zip(bhs.tolist(), qts.tolist()):

@@ -189,6 +189,23 @@ def test_varlen_rows_are_independent_of_neighbours():
         assert same == (s != 1), f"sequence {s}"
 
 
+@pytest.mark.parametrize("nseq", [64, 65])
+def test_varlen_many_sequences(nseq):
+    """Up to 64 packed sequences are walked longest first (the kernel ranks
+    the table), more in table order: both sides of that limit, with ties and
+    empty sequences, against the oracle."""
+    g = np.random.Generator(np.random.PCG64(79_000 + nseq))
+    lens = g.integers(1, 300, size=nseq)
+    lens[g.random(nseq) < 0.1] = 0
+    lens[:4] = 150                                   # ties
+    q, k, v, cu = make_packed(79_100 + nseq, lens.tolist(), 2, 1, 64)
+    for causal in (False, True):
+        log(f"case varlen {nseq} sequences causal={causal}")
+        O, L = gpu_varlen(q, k, v, cu, causal, scale=0.125)
+        Oref, Lref = oracle.attention_varlen(q, k, v, cu, 0.125, window=eff_window(causal, None))
+        check(O, L, Oref, Lref, f"varlen {nseq} sequences causal={causal}")
+
+
 def test_varlen_max_seqlen_given():
     lens = [100, 300, 50]
     q, k, v, cu = make_packed(77_000, lens, 2, 1, 128)
