@@ -7,12 +7,14 @@ B=4, H=8, S=4096, D=64 non-causal fp16 workload, inputs already resident in HBM.
 Prints one JSON line:
 
     value      FLOP rate, 4*B*H*S^2*D FLOPs (halved when causal) / average step time
+               over K back-to-back steps timed by one pair of HIP events
     roofline   the kernel against the MI355X dense fp16 MFMA peak (2516.6 TFLOP/s),
-               its duration taken with HIP events on the launch stream
+               its duration taken with HIP events around each launch on the
+               launch stream, in a second pass of the same K steps
     cpu_baseline  the fp64 CPU oracle timed on a bounded sample of the same
                workload on this host's cores (a reported baseline, not a target)
 
-    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload 2] [--causal]
+    python bench.py [--gpus 1] [--steps 200] [--warmup 200] [--workload 2] [--causal]
     python bench.py --feature {gqa,mqa,window,varlen,dropout} [--causal]
 
 --feature times one of the production-feature workloads (GQA/MQA, local
@@ -210,8 +212,10 @@ def gemm_calibration(reps: int) -> None:
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    # The GPU clock needs on the order of 100 back-to-back launches to settle;
+    # steps timed right after a short warmup run 5-20 % slow.
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--causal", action="store_true", help="run the causal variant of the workload")
     ap.add_argument("--feature", choices=["gqa", "mqa", "window", "varlen", "dropout"], default=None,
@@ -289,11 +293,12 @@ def main():
     torch.cuda.synchronize()
     log("bench: warmup done")
 
-    # Per-launch events on the launch stream give the kernel duration; the outer
-    # pair gives the step time.
+    # Two timed passes of the same K steps on the launch stream. The first has
+    # only the outer pair of events and gives the step time (value); the second
+    # records an event pair around every launch and gives the kernel duration
+    # (roofline.achieved). Per-launch events are kept out of the first pass
+    # because each one adds a gap of several microseconds between kernels.
     scrub = torch.empty(512 << 20, dtype=torch.uint8, device=dev) if args.cold else None
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -301,13 +306,22 @@ def main():
     for i in range(args.steps):
         if scrub is not None:
             scrub.fill_(i & 255)
-        starts[i].record(stream)
         step()
-        ends[i].record(stream)
     t1.record(stream)
     torch.cuda.synchronize()
     total_ms = t0.elapsed_time(t1)
     ms_per_step = total_ms / args.steps
+
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        if scrub is not None:
+            scrub.fill_(i & 255)
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
     kern_ms = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
     kern_avg_ms = sum(kern_ms) / len(kern_ms)
     log(f"bench: {ms_per_step * 1e3:.1f} us/step, kernel avg {kern_avg_ms * 1e3:.1f} us "
