@@ -192,7 +192,7 @@ def gemm_calibration(reps: int) -> None:
         a = torch.randn(batch, m, k, device=dev, dtype=dt, generator=g)
         b = torch.randn(batch, k, n, device=dev, dtype=dt, generator=g)
         fn = (lambda: torch.matmul(a[0], b[0])) if batch == 1 else (lambda: torch.bmm(a, b))
-        for _ in range(3):
+        for _ in range(50):  # lets the clock settle, as for the attention kernel
             fn()
         torch.cuda.synchronize()
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
