@@ -13,7 +13,7 @@ def pytest_configure(config):
 
 
 def pytest_collection_modifyitems(config, items):
-    # GPU tests are skipped, not failed, where no GPU is visible; on a GPU machine they
+    # GPU tests are skipped, not failed, where no GPU is visible; on a machine with an MI355X they
     # run and call the HIP library through its C ABI.
     try:
         import torch
