@@ -152,8 +152,9 @@ def forward(q, k, v, causal: bool = False, scale: float | None = None, out=None,
     lse = _output(lse, (B, H, S), torch.float32, q, "lse")
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
-    st = fa2_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, S, D,
-                 int(bool(causal)), scale, stream)
+    with torch.cuda.device(q.device):  # the library launches on the current device
+        st = fa2_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, S, D,
+                     int(bool(causal)), scale, stream)
     if st != FA2_OK:
         raise FA2Error(st)
     return out, lse
@@ -178,8 +179,9 @@ def forward_ex(q, k, v, causal: bool = False, window=None, dropout_p: float = 0.
     lse = _output(lse, (B, H, S), torch.float32, q, "lse")
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
-    st = fa2_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, H_kv, S, D,
-                    wl, wr, dropout_p, seed, offset, scale, stream)
+    with torch.cuda.device(q.device):
+        st = fa2_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, H_kv, S,
+                        D, wl, wr, dropout_p, seed, offset, scale, stream)
     if st != FA2_OK:
         raise FA2Error(st)
     return out, lse
@@ -215,9 +217,10 @@ def forward_varlen(q, k, v, cu_seqlens, max_seqlen: int | None = None, causal: b
     lse = _output(lse, (H, total), torch.float32, q, "lse")
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
-    st = fa2_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-                        cu_seqlens.data_ptr(), num_seqs, total, max_seqlen, H, H_kv, D, wl, wr, dropout_p, seed,
-                        offset, scale, stream)
+    with torch.cuda.device(q.device):
+        st = fa2_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                            cu_seqlens.data_ptr(), num_seqs, total, max_seqlen, H, H_kv, D, wl, wr, dropout_p,
+                            seed, offset, scale, stream)
     if st != FA2_OK:
         raise FA2Error(st)
     return out, lse

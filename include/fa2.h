@@ -86,7 +86,9 @@ typedef enum {
  *   scale    softmax scale applied to q_i . k_j; finite and > 0 (the kernel
  *            takes the row maximum on unscaled scores and scales afterwards,
  *            which is exact only for a positive scale).
- *   stream   a hipStream_t, or NULL for the default stream.
+ *   stream   a hipStream_t of the current HIP device (the pointers are that
+ *            device's memory), or NULL for its default stream. The device
+ *            check and the launch use the current device.
  *
  * Ownership: the caller allocates and owns every buffer; the library allocates
  * no device memory and keeps no state besides per-device "is gfx950" and
