@@ -667,15 +667,25 @@ void fa2_fwd_kernel(KernelArgs a) {
         // Source lane l16 of group g points at row 4g + l16/4 (+16 for the second
         // half) and columns 16*db + 4*(l16%4) .. +3; the transposing read returns
         // V[32kc + 4g + e][16db + l16] in element e.
+        auto read_v = [&](int kc, int db) __attribute__((always_inline)) {
+            const char* p0 = ldsV + (rv ^ (db << 5)) + kc * 32 * D * 2;
+            const s16x4 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p0);
+            const s16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0 + 16 * D * 2));
+            const half4 h0 = __builtin_bit_cast(half4, t0);
+            const half4 h1 = __builtin_bit_cast(half4, t1);
+            return half8{h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
+        };
+        // At D=128 (2 waves per SIMD, registers to spare) the V fragments of the
+        // first chunk are read here, before the softmax, so that their LDS
+        // latency hides under its VALU work. At D=64 the registers are not there.
+        constexpr int VPRE = (D == 128) ? DB : 0;
+        half8 vpre[VPRE > 0 ? VPRE : 1];
+#pragma unroll
+        for (int i = 0; i < VPRE; ++i) vpre[i] = read_v(0, i);
         auto pv_chunk = [&](int kc) __attribute__((always_inline)) {
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
-                const char* p0 = ldsV + (rv ^ (db << 5)) + kc * 32 * D * 2;
-                const s16x4 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p0);
-                const s16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0 + 16 * D * 2));
-                const half4 h0 = __builtin_bit_cast(half4, t0);
-                const half4 h1 = __builtin_bit_cast(half4, t1);
-                const half8 va = half8{h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
+                const half8 va = (kc == 0 && db < VPRE) ? vpre[db] : read_v(kc, db);
 #pragma unroll
                 for (int qb = 0; qb < QB; ++qb)
                     oacc[db][qb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb[qb][kc], oacc[db][qb], 0, 0, 0);
