@@ -495,6 +495,16 @@ void fa2_fwd_kernel(KernelArgs a) {
         l_run[qb] = 0.f;
     }
     const half2 kOnes2 = half2{(_Float16)1.0f, (_Float16)1.0f};
+    // All-ones MFMA operand of the matrix-unit row sums, kept live at D=64.
+    constexpr bool KEEP_ONES = ROWSUM_MFMA && D == 64;
+    half8 kOnesKeep = half8{};
+    if (KEEP_ONES) {
+        uint32_t o2[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) asm volatile("v_mov_b32 %0, 0x3c003c00" : "=v"(o2[i]));
+        typedef uint32_t u32x4w __attribute__((ext_vector_type(4)));
+        kOnesKeep = __builtin_bit_cast(half8, u32x4w{o2[0], o2[1], o2[2], o2[3]});
+    }
     bool fresh = true;  // no tile computed by this wave yet
 
     // LDS read offsets (bytes) that do not depend on the tile: the K swizzle of
@@ -704,14 +714,18 @@ void fa2_fwd_kernel(KernelArgs a) {
             if (ROWSUM_MFMA) {
                 // the tile's full row sums on the matrix unit (each lane gets
                 // its query's sum over all BN keys): an MFMA with an all-ones
-                // A operand sums the B operand (P^T) over its 32 keys. The
-                // constant is rebuilt here with volatile moves so that it is
-                // not kept live across the loop (it would be spilled).
-                uint32_t one2[4];
+                // A operand sums the B operand (P^T) over its 32 keys. At D=64
+                // the constant stays in registers for the whole scan; at D=128
+                // it is rebuilt here with volatile moves, which measured
+                // faster there than keeping it live.
+                half8 kOnes8 = kOnesKeep;
+                if (!KEEP_ONES) {
+                    uint32_t one2[4];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) asm volatile("v_mov_b32 %0, 0x3c003c00" : "=v"(one2[i]));
-                typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
-                const half8 kOnes8 = __builtin_bit_cast(half8, u32x4v{one2[0], one2[1], one2[2], one2[3]});
+                    for (int i = 0; i < 4; ++i) asm volatile("v_mov_b32 %0, 0x3c003c00" : "=v"(one2[i]));
+                    typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+                    kOnes8 = __builtin_bit_cast(half8, u32x4v{one2[0], one2[1], one2[2], one2[3]});
+                }
 #pragma unroll
                 for (int qb = 0; qb < QB; ++qb) {
                     f32x4 ls = f32x4{0.f, 0.f, 0.f, 0.f};
