@@ -662,11 +662,21 @@ void fa2_fwd_kernel(KernelArgs a) {
                 const auto s0 = __builtin_amdgcn_permlane16_swap(r.w[0], r.w[2], false, false);
                 const auto s1 = __builtin_amdgcn_permlane16_swap(r.w[1], r.w[3], false, false);
                 const uint32_t w[4] = {s0[0], s1[0], s0[1], s1[1]};
+                // Keep mask per 16-bit half, 0xFFFF for draw >= drop_thr and 0
+                // otherwise, in three packed 16-bit integer ops per word:
+                // sat(thr - draw) is 0 exactly for kept keys, min(., 1) - 1
+                // (wrapping) maps 0 to 0xFFFF and 1 to 0. drop_thr <= 0xFFFF, and
+                // drop_thr = 0 keeps every key.
+                const uint32_t thr2 = a.drop_thr * 0x00010001u;
+                const uint32_t one2 = 0x00010001u;
                 uint32_t m[4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    m[e] = ((w[e] & 0xFFFFu) >= a.drop_thr ? 0x0000FFFFu : 0u) |
-                           ((w[e] >> 16) >= a.drop_thr ? 0xFFFF0000u : 0u);
+                for (int e = 0; e < 4; ++e) {
+                    uint32_t over, m01;
+                    asm("v_pk_sub_u16 %0, %1, %2 clamp" : "=v"(over) : "v"(thr2), "v"(w[e]));
+                    asm("v_pk_min_u16 %0, %1, %2" : "=v"(m01) : "v"(over), "v"(one2));
+                    asm("v_pk_sub_u16 %0, %1, %2" : "=v"(m[e]) : "v"(m01), "v"(one2));
+                }
                 typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
                 u32x4v bits = __builtin_bit_cast(u32x4v, pb[qb][kc]);
                 bits &= u32x4v{m[0], m[1], m[2], m[3]};

@@ -464,6 +464,28 @@ def test_malformed_sequence_tables_stay_in_bounds(D):
         emulate(len(cu) - 1, 2, S, D, True, cu=cu, total=total)
 
 
+def _packed_keep_mask(word, thr):
+    """The kernel's keep mask of one 32-bit word of two 16-bit draws, as its
+    three packed 16-bit ops compute it: v_pk_sub_u16 with clamp (thr - draw,
+    saturating at 0), v_pk_min_u16 with 1, v_pk_sub_u16 of 1 (wrapping)."""
+    halves = np.stack([word & 0xFFFF, word >> 16]).astype(np.int64)
+    over = np.maximum(thr - halves, 0)
+    m = (np.minimum(over, 1) - 1) & 0xFFFF
+    return (m[0] | (m[1] << 16)).astype(np.uint32)
+
+
+@pytest.mark.parametrize("thr", [0, 1, 2, 6553, 32767, 32768, 65534, 65535])
+def test_dropout_keep_mask_bit_trick(thr):
+    """For every 16-bit draw in either half: 0xFFFF when draw >= thr (kept),
+    0 otherwise, the other half independent."""
+    d = np.arange(1 << 16, dtype=np.uint32)
+    for other in (0, 1, thr, 0xFFFF):
+        for word, shift in ((d | (np.uint32(other) << 16), 0), ((d << 16) | np.uint32(other), 16)):
+            m = _packed_keep_mask(word, thr)
+            assert np.array_equal((m >> shift) & 0xFFFF, np.where(d >= thr, 0xFFFF, 0).astype(np.uint32))
+            assert np.all(((m >> (16 - shift)) & 0xFFFF) == (0xFFFF if other >= thr else 0))
+
+
 def test_dropout_counter_names_the_register_key():
     """Element x of P^T register pb[qb][kc] of lane (l16, g) holds key
     j = k0 + 32kc + 16(x//4) + 4g + x%4 (the S^T accumulator order). The
