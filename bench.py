@@ -13,8 +13,11 @@ Prints one JSON line:
                launch stream, in a second pass of the same K steps
     cpu_baseline  the fp64 CPU oracle timed on a bounded sample of the same
                workload on this host's cores (a reported baseline, not a target)
+    graph_timing  per-launch time of N launches captured in one HIP graph,
+               median and range over R replays (the pages' own timing method;
+               a cross-check, not the value)
 
-    python bench.py [--gpus 1] [--steps 200] [--warmup 200] [--workload 2] [--causal]
+    python bench.py [--gpus 1] [--steps 200] [--warmup 200] [--workload 2] [--causal] [--graph 100]
     python bench.py --feature {gqa,mqa,window,varlen,dropout} [--causal]
 
 --feature times one of the production-feature workloads (GQA/MQA, local
@@ -121,10 +124,10 @@ def feature_setup(key: str, causal: bool, dev):
         lse = torch.empty((f.H, total), dtype=torch.float32, device=dev)
         max_len = int(np.max(np.diff(cu)))
 
-        def step():
+        def step(sp=stream):
             st = fa2.fa2_fwd_varlen(qt.data_ptr(), kt.data_ptr(), vt.data_ptr(), o.data_ptr(), lse.data_ptr(),
                                     cut.data_ptr(), len(cu) - 1, total, max_len, f.H, f.H_kv, f.D, wl, wr,
-                                    f.dropout_p, f.seed, 0, f.scale, stream)
+                                    f.dropout_p, f.seed, 0, f.scale, sp)
             if st != 0:
                 raise fa2.FA2Error(st)
         pairs = f.H * sum(admitted_pairs(int(L), wl, wr, causal) for L in np.diff(cu))
@@ -149,9 +152,9 @@ def feature_setup(key: str, causal: bool, dev):
         o = torch.empty_like(qt)
         lse = torch.empty((f.B, f.H, f.S), dtype=torch.float32, device=dev)
 
-        def step():
+        def step(sp=stream):
             st = fa2.fa2_fwd_ex(qt.data_ptr(), kt.data_ptr(), vt.data_ptr(), o.data_ptr(), lse.data_ptr(), f.B,
-                                f.H, f.H_kv, f.S, f.D, wl, wr, f.dropout_p, f.seed, 0, f.scale, stream)
+                                f.H, f.H_kv, f.S, f.D, wl, wr, f.dropout_p, f.seed, 0, f.scale, sp)
             if st != 0:
                 raise fa2.FA2Error(st)
         pairs = f.B * f.H * admitted_pairs(f.S, wl, wr, causal)
@@ -225,6 +228,10 @@ def main():
                     help="write a 512 MiB buffer between launches so inputs come from HBM, not L2/MALL; "
                          "value is then the kernel rate (the step time would include the eviction)")
     ap.add_argument("--cpu-stride", type=int, default=1, help="oracle sample: every n-th row (1 = all rows)")
+    ap.add_argument("--graph", type=int, default=100, metavar="N",
+                    help="also time N launches captured in one HIP graph, replayed --graph-rounds times "
+                         "(median, min, max per launch in graph_timing); 0 skips it")
+    ap.add_argument("--graph-rounds", type=int, default=9)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the benchmark, run 10 plain device-to-device copies of MIB MiB "
                          "(the reference kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -279,7 +286,7 @@ def main():
         sp = stream.cuda_stream
         ptrs = (qt.data_ptr(), kt.data_ptr(), vt.data_ptr(), o.data_ptr(), lse.data_ptr())
 
-        def step():
+        def step(sp=sp):
             st = fa2.fa2_fwd(*ptrs, w.B, w.H, w.S, w.D, int(causal), w.scale, sp)
             if st != 0:
                 raise fa2.FA2Error(st)
@@ -327,6 +334,41 @@ def main():
     log(f"bench: {ms_per_step * 1e3:.1f} us/step, kernel avg {kern_avg_ms * 1e3:.1f} us "
         f"(min {kern_ms[0] * 1e3:.1f}, median {kern_ms[len(kern_ms) // 2] * 1e3:.1f})")
 
+    # Graph timing, as the pages time their kernels: N launches captured in one
+    # HIP graph on a side stream, one untimed replay, then R timed replays; the
+    # per-launch time of each replay, median and range. A cross-check of the
+    # step time without per-launch host overhead; warm cache only.
+    graph_timing = None
+    if args.graph > 0:
+        side = torch.cuda.Stream(device=dev)
+        side.wait_stream(stream)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(graph, stream=side):
+                for _ in range(args.graph):
+                    step(side.cuda_stream)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        per = []
+        for _ in range(args.graph_rounds):
+            g0 = torch.cuda.Event(enable_timing=True)
+            g1 = torch.cuda.Event(enable_timing=True)
+            g0.record(stream)
+            graph.replay()
+            g1.record(stream)
+            torch.cuda.synchronize()
+            per.append(g0.elapsed_time(g1) / args.graph)
+        per.sort()
+        med = per[len(per) // 2]
+        graph_timing = {"launches_per_graph": args.graph, "rounds": args.graph_rounds,
+                        "median_us": round(med * 1e3, 2), "min_us": round(per[0] * 1e3, 2),
+                        "max_us": round(per[-1] * 1e3, 2),
+                        "tflops_at_median": round(flops / (med * 1e-3) / 1e12, 2)}
+        log(f"bench: graph of {args.graph} launches, {args.graph_rounds} replays: median {med * 1e3:.1f} us "
+            f"per launch (min {per[0] * 1e3:.1f}, max {per[-1] * 1e3:.1f})")
+        del graph
+
     achieved = flops / (kern_avg_ms * 1e-3) / 1e12
     value = achieved if args.cold else flops / (ms_per_step * 1e-3) / 1e12
     traffic = None if args.feature else measured_traffic(args.workload, causal)
@@ -367,6 +409,7 @@ def main():
                    "pct_of_fp16_mfma_peak": round(100 * value / MFMA_F16_PEAK_TFLOPS, 2)},
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "graph_timing": graph_timing,
     }
     print(json.dumps(rec), flush=True)
 

@@ -93,10 +93,20 @@ def test_bench_json_line():
     c = d["cpu_baseline"]
     assert c["kind"] == "oracle" and c["unit"] == "TFLOP/s" and c["cores"] >= 1 and c["value"] > 0
     assert "every 256th query row" in c["sample"]
+    gt = d["graph_timing"]
+    assert gt["launches_per_graph"] == 100 and gt["rounds"] == 9
+    assert 0 < gt["min_us"] <= gt["median_us"] <= gt["max_us"]
+    assert gt["tflops_at_median"] == pytest.approx(flops / (gt["median_us"] * 1e-6) / 1e12, rel=1e-3)
+    # the graph's per-launch time and the back-to-back step time measure the same kernel
+    assert gt["median_us"] == pytest.approx(d["ms_per_step"] * 1e3, rel=0.35)
 
 
 @pytest.mark.gpu
 def test_bench_feature_line():
-    d = _run_bench(["--feature", "varlen", "--causal", "--steps", "10", "--warmup", "10", "--no-cpu-baseline"])
+    d = _run_bench(["--feature", "varlen", "--causal", "--steps", "10", "--warmup", "10", "--no-cpu-baseline",
+                    "--graph", "20", "--graph-rounds", "3"])
     assert d["value"] > 0 and d["cpu_baseline"] is None and d["roofline"]["traffic"] is None
+    assert d["graph_timing"]["launches_per_graph"] == 20 and d["graph_timing"]["median_us"] > 0
     assert d["config"]["causal"] is True and d["config"]["sequences"] == 24
+    d0 = _run_bench(["--workload", "1", "--steps", "5", "--warmup", "5", "--no-cpu-baseline", "--graph", "0"])
+    assert d0["graph_timing"] is None
