@@ -582,16 +582,16 @@ void fa2_fwd_kernel(KernelArgs a) {
         // Probabilities are taken against the running reference m (held as
         // mc_run = m*c): p = 2^(s*c - m*c). l and o always use the same
         // reference per row, so O = o/l and LSE = scale*m + ln l hold for any
-        // reference; the
-        // reference only has to keep every p representable in fp16. The
-        // common path therefore skips the row max: it exponentiates against
-        // the current reference and accepts the result if the row sum of the
-        // fp16 p (a lane's partial sum, or with the matrix-unit sums the
-        // tile's full row sum) stays below 2^15, so no p overflowed. The
-        // first tile, or a chunk that fails the check, takes the row max
-        // (combined over the 4 lanes of a query), moves the reference to
-        // max(m, max), rescales o and l by alpha = 2^((m_old - m_new)*c)
-        // and exponentiates again: the update of the online softmax.
+        // reference; it only has to keep every p representable in fp16. The
+        // common path therefore skips the row max: it exponentiates the tile
+        // against the current reference and accepts the result if the row
+        // sums of the fp16 p (a lane's partial sums, or with the matrix-unit
+        // sums the tile's full row sums) stay below 2^15, so no p overflowed.
+        // A wave's first tile, or a tile that fails the check for any of its
+        // rows, takes the row max (combined over the 4 lanes of a query),
+        // moves the reference to max(m, max), rescales o and l by
+        // alpha = 2^((m_old - m_new)*c) and exponentiates again: the update
+        // of the online softmax.
         half8 pb[QB][NKC];
 
         // p of 32-key chunk kc (16-key blocks 2kc, 2kc+1) of query block qb, as
