@@ -652,7 +652,12 @@ void fa2_fwd_kernel(KernelArgs a) {
         // words it needs. Kept probabilities are scaled by 1/(1-p) in the
         // epilogue.
         auto drop_chunk = [&](int kc) __attribute__((always_inline)) {
-            const uint32_t group = (uint32_t)((k0 + 32 * kc) >> 3) + 2u * (uint32_t)(g & 1) + (uint32_t)(g >> 1);
+            uint32_t group = (uint32_t)((k0 + 32 * kc) >> 3) + 2u * (uint32_t)(g & 1) + (uint32_t)(g >> 1);
+            // Opaque to the optimiser: the counter grows linearly with the
+            // tile, and loop strength reduction otherwise keeps the first
+            // round's 64-bit product for every chunk position of a stage live
+            // across the scan (16 VGPRs), which spills.
+            asm volatile("" : "+v"(group));
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb) {
                 const uint32_t qrow = (uint32_t)(qw0 + 16 * qb + l16);
