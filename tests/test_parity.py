@@ -252,6 +252,35 @@ def test_wide_grid_sampled():
         check(O.reshape(-1, D)[rows], L.reshape(-1)[rows], Oref, Lref, f"wide grid causal={causal}")
 
 
+def test_grid_beyond_2pow22_workgroups():
+    """More than 2^22 workgroups (B4097 H1024 S1: 4,195,328), where the launch
+    splits the grid over (x, y). With one key per row the softmax weight is
+    exactly 1, so O must equal V exactly on every row (as numbers: a -0.0 in V
+    comes out as +0.0, since the accumulator starts at +0.0); LSE and O are
+    also checked against the oracle on sampled rows on both sides of 2^22, and
+    the causal kernel must agree."""
+    import attention_forward_fa2_amd as fa2
+    B, H, S, D = 4097, 1024, 1, 64
+    cfg = fa2.fa2_kernel_config(B, H, S, D, 0)
+    assert cfg["blocks"] > (1 << 22)
+    log(f"case grid beyond 2^22: B={B} H={H} S={S} D={D} {cfg}")
+    q, k, v = make_random(48_000, B, H, S, D)
+    g = np.random.Generator(np.random.PCG64(48_001))
+    n = B * H * S
+    rows = np.unique(np.concatenate([g.integers(0, n, size=64), np.arange(n - 8, n),
+                                     np.arange((1 << 22) - 8, (1 << 22) + 8)]))
+    Oref, Lref = oracle.attention_rows(q, k, v, False, 0.125, rows)
+    for causal in (False, True):
+        O, L = gpu_forward(q, k, v, causal, 0.125)
+        bad = np.nonzero(np.any(O.reshape(-1, D) != v.reshape(-1, D), axis=1))[0]
+        if bad.size:
+            log(f"  causal={causal}: {bad.size} of {n} rows differ from V; first {bad[:8].tolist()}, "
+                f"last {bad[-8:].tolist()}; max |O - V| {np.abs(O.reshape(-1, D)[bad].astype(np.float64) - v.reshape(-1, D)[bad]).max():.3e}")
+        assert bad.size == 0, f"causal={causal}: O differs from V on {bad.size} rows"
+        check(O.reshape(-1, D)[rows], L.reshape(-1)[rows], Oref, Lref, f"grid beyond 2^22 causal={causal}")
+        del O, L
+
+
 @pytest.mark.parametrize("D,B,H", [(64, 4, 8), (128, 1, 16)])
 def test_one_round_causal_every_workgroup(D, B, H):
     """Causal grids resident in one round (half-height workgroups, serpentine
