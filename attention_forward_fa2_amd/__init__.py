@@ -117,6 +117,8 @@ def _check_inputs(q, k, v):
         raise ValueError("q, k, v must be contiguous")
     if not (q.is_cuda and k.is_cuda and v.is_cuda):
         raise ValueError("q, k, v must be GPU tensors")
+    if k.device != q.device or v.device != q.device:
+        raise ValueError(f"q, k, v must be on one device, got {q.device}, {k.device}, {v.device}")
     if k.shape != v.shape:
         raise ValueError(f"k and v must have the same shape, got {tuple(k.shape)} {tuple(v.shape)}")
 

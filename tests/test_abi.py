@@ -251,6 +251,21 @@ def test_forward_rejects_bad_tensors():
         fa2.forward_varlen(p, p, p, cu.long())
 
 
+def test_inputs_on_different_devices_are_rejected():
+    """The kernel reads every tensor from the device of q; stand-ins for GPU
+    tensors on two devices (no second GPU is needed to check the host side)."""
+    import types
+    import torch
+
+    def fake(dev):
+        return types.SimpleNamespace(dtype=torch.float16, is_cuda=True, device=torch.device(dev),
+                                     shape=(1, 1, 8, 64), is_contiguous=lambda: True)
+    fa2._check_inputs(fake("cuda:0"), fake("cuda:0"), fake("cuda:0"))
+    for k_dev, v_dev in (("cuda:1", "cuda:0"), ("cuda:0", "cuda:1")):
+        with pytest.raises(ValueError, match="one device"):
+            fa2._check_inputs(fake("cuda:0"), fake(k_dev), fake(v_dev))
+
+
 def test_no_fallback_when_library_missing(tmp_path):
     with pytest.raises(ImportError):
         fa2.load_library(str(tmp_path / "libfa2.so"))
