@@ -521,19 +521,20 @@ void fa2_fwd_kernel(KernelArgs a) {
         return 2u * (r0 * D + 8 * (((l16 & 3) >> 1) ^ swz_v<D>(r0)) + 4 * (l16 & 1));
     }();
 
-    // One compute tile: keys k0 .. k0+BN-1, K and V at the given LDS addresses.
-    auto compute_tile = [&](const int k0, const char* const ldsK, const char* const ldsV)
-                            __attribute__((always_inline)) {
+    // Per-tile register arrays: the S^T accumulators and the fp16 P^T operands.
+    typedef f32x4 SAccT[QB][NKB];
+    typedef half8 PBT[QB][NKC];
 
-        // The per-k-step and per-column-block offsets are derived from the two
-        // bases inside the tile; the empty asm keeps the compiler from
-        // hoisting them out of the loop into registers of their own.
-        uint32_t rk = rdK0, rv = rdV0;
-        asm volatile("" : "+v"(rk), "+v"(rv));
-
-        // ---- S^T = K Q^T on MFMA ----
+    // ---- S^T = K Q^T on MFMA for the compute tile at k0 (K at ldsK), then the
+    // masks: keys past the end, after the query (causal), outside the window
+    // (local) ----
+    auto scores = [&](const int k0, const char* const ldsK, SAccT& sacc) __attribute__((always_inline)) {
+        // The per-k-step offsets are derived from the base inside the tile; the
+        // empty asm keeps the compiler from hoisting them out of the loop into
+        // registers of their own.
+        uint32_t rk = rdK0;
+        asm volatile("" : "+v"(rk));
         if (FA2_SETPRIO) __builtin_amdgcn_s_setprio(FA2_PRIO_QK);
-        f32x4 sacc[QB][NKB];
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
@@ -556,8 +557,6 @@ void fa2_fwd_kernel(KernelArgs a) {
         }
         if (FA2_SETPRIO) __builtin_amdgcn_s_setprio(FA2_PRIO_SM);
 
-        // ---- masks: keys past the end, after the query (causal), outside the
-        // window (local) ----
         bool need_mask = k0 + BN > len;
         if (MASK == kCausal) need_mask |= k0 + BN - 1 > qw0;
         if (MASK == kWindow) need_mask |= (k0 < qw0 + QW - 1 - a.wl) || (k0 + BN - 1 > qw0 + a.wr);
@@ -577,204 +576,225 @@ void fa2_fwd_kernel(KernelArgs a) {
                     }
             }
         }
+    };
 
-        // ---- online softmax update ----
-        // Probabilities are taken against the running reference m (held as
-        // mc_run = m*c): p = 2^(s*c - m*c). l and o always use the same
-        // reference per row, so O = o/l and LSE = scale*m + ln l hold for any
-        // reference; it only has to keep every p representable in fp16. The
-        // common path therefore skips the row max: it exponentiates the tile
-        // against the current reference and accepts the result if the row
-        // sums of the fp16 p (a lane's partial sums, or with the matrix-unit
-        // sums the tile's full row sums) stay below 2^15, so no p overflowed.
-        // A wave's first tile, or a tile that fails the check for any of its
-        // rows, takes the row max (combined over the 4 lanes of a query),
-        // moves the reference to max(m, max), rescales o and l by
-        // alpha = 2^((m_old - m_new)*c) and exponentiates again: the update
-        // of the online softmax.
-        half8 pb[QB][NKC];
+    // ---- online softmax update ----
+    // Probabilities are taken against the running reference m (held as
+    // mc_run = m*c): p = 2^(s*c - m*c). l and o always use the same
+    // reference per row, so O = o/l and LSE = scale*m + ln l hold for any
+    // reference; it only has to keep every p representable in fp16. The
+    // common path therefore skips the row max: it exponentiates the tile
+    // against the current reference and accepts the result if the row
+    // sums of the fp16 p (a lane's partial sums, or with the matrix-unit
+    // sums the tile's full row sums) stay below 2^15, so no p overflowed.
+    // A wave's first tile, or a tile that fails the check for any of its
+    // rows, takes the row max (combined over the 4 lanes of a query),
+    // moves the reference to max(m, max), rescales o and l by
+    // alpha = 2^((m_old - m_new)*c) and exponentiates again: the update
+    // of the online softmax.
 
-        // p of 32-key chunk kc (16-key blocks 2kc, 2kc+1) of query block qb, as
-        // the fp16 B operand of the PV product, and its partial row sum (over
-        // the fp16 values, before dropout: the softmax normaliser counts every
-        // admissible key).
-        auto exp_chunk = [&](int qb, int kc, float& rsum) __attribute__((always_inline)) {
-            const float mc = mc_run[qb];
-            const f32x4 lo = sacc[qb][2 * kc], hi = sacc[qb][2 * kc + 1];
-            half2 h[4];
+    // p of 32-key chunk kc (16-key blocks 2kc, 2kc+1) of query block qb, as
+    // the fp16 B operand of the PV product, and its partial row sum (over
+    // the fp16 values, before dropout: the softmax normaliser counts every
+    // admissible key).
+    auto exp_chunk = [&](const SAccT& sacc, PBT& pb, int qb, int kc, float& rsum) __attribute__((always_inline)) {
+        const float mc = mc_run[qb];
+        const f32x4 lo = sacc[qb][2 * kc], hi = sacc[qb][2 * kc + 1];
+        half2 h[4];
 #pragma unroll
-            for (int e = 0; e < 2; ++e) {
-                const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(lo[2 * e], a.c, -mc));
-                const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(lo[2 * e + 1], a.c, -mc));
-                const float p2 = __builtin_amdgcn_exp2f(__builtin_fmaf(hi[2 * e], a.c, -mc));
-                const float p3 = __builtin_amdgcn_exp2f(__builtin_fmaf(hi[2 * e + 1], a.c, -mc));
-                h[e] = half2{(_Float16)p0, (_Float16)p1};
-                h[2 + e] = half2{(_Float16)p2, (_Float16)p3};
-            }
-            if (!ROWSUM_MFMA) {
+        for (int e = 0; e < 2; ++e) {
+            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(lo[2 * e], a.c, -mc));
+            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(lo[2 * e + 1], a.c, -mc));
+            const float p2 = __builtin_amdgcn_exp2f(__builtin_fmaf(hi[2 * e], a.c, -mc));
+            const float p3 = __builtin_amdgcn_exp2f(__builtin_fmaf(hi[2 * e + 1], a.c, -mc));
+            h[e] = half2{(_Float16)p0, (_Float16)p1};
+            h[2 + e] = half2{(_Float16)p2, (_Float16)p3};
+        }
+        if (!ROWSUM_MFMA) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) rsum = __builtin_amdgcn_fdot2(h[e], kOnes2, rsum, false);
-            }
-            pb[qb][kc] = half8{h[0][0], h[0][1], h[1][0], h[1][1], h[2][0], h[2][1], h[3][0], h[3][1]};
-        };
-        // Row max over 16-key blocks kb0 .. kb1-1, combined over the 4 lanes of a query.
-        auto row_max = [&](int qb, int kb0, int kb1) __attribute__((always_inline)) {
-            float a0 = fmaxf(sacc[qb][kb0][0], sacc[qb][kb0][1]);
-            float a1 = fmaxf(sacc[qb][kb0][2], sacc[qb][kb0][3]);
-            for (int kb = kb0 + 1; kb < kb1; ++kb) {
-                a0 = fmaxf(a0, fmaxf(sacc[qb][kb][0], sacc[qb][kb][1]));
-                a1 = fmaxf(a1, fmaxf(sacc[qb][kb][2], sacc[qb][kb][3]));
-            }
-            return max_xor32(max_xor16(fmaxf(a0, a1)));
-        };
-        // Move the reference of query block qb up to the raw score mx (if
-        // higher), rescaling o and l. Rounding is monotonic, so max(m*c, mx*c)
-        // is the scaled maximum exactly.
-        auto move_reference = [&](int qb, float mx) __attribute__((always_inline)) {
-            const float m_new = fmaxf(mc_run[qb], mx * a.c);
-            const float alpha = __builtin_amdgcn_exp2f(mc_run[qb] - m_new);
-            mc_run[qb] = m_new;
-            l_run[qb] *= alpha;
+            for (int e = 0; e < 4; ++e) rsum = __builtin_amdgcn_fdot2(h[e], kOnes2, rsum, false);
+        }
+        pb[qb][kc] = half8{h[0][0], h[0][1], h[1][0], h[1][1], h[2][0], h[2][1], h[3][0], h[3][1]};
+    };
+    // Row max over 16-key blocks kb0 .. kb1-1, combined over the 4 lanes of a query.
+    auto row_max = [&](const SAccT& sacc, int qb, int kb0, int kb1) __attribute__((always_inline)) {
+        float a0 = fmaxf(sacc[qb][kb0][0], sacc[qb][kb0][1]);
+        float a1 = fmaxf(sacc[qb][kb0][2], sacc[qb][kb0][3]);
+        for (int kb = kb0 + 1; kb < kb1; ++kb) {
+            a0 = fmaxf(a0, fmaxf(sacc[qb][kb][0], sacc[qb][kb][1]));
+            a1 = fmaxf(a1, fmaxf(sacc[qb][kb][2], sacc[qb][kb][3]));
+        }
+        return max_xor32(max_xor16(fmaxf(a0, a1)));
+    };
+    // Move the reference of query block qb up to the raw score mx (if
+    // higher), rescaling o and l. Rounding is monotonic, so max(m*c, mx*c)
+    // is the scaled maximum exactly.
+    auto move_reference = [&](int qb, float mx) __attribute__((always_inline)) {
+        const float m_new = fmaxf(mc_run[qb], mx * a.c);
+        const float alpha = __builtin_amdgcn_exp2f(mc_run[qb] - m_new);
+        mc_run[qb] = m_new;
+        l_run[qb] *= alpha;
 #pragma unroll
-            for (int db = 0; db < DB; ++db) oacc[db][qb] *= alpha;
-        };
+        for (int db = 0; db < DB; ++db) oacc[db][qb] *= alpha;
+    };
 
-        // ---- dropout on P: zero the probabilities of dropped keys ----
-        // Key j of query row i (both within the sequence) of head (b, h) takes
-        // 16-bit draw j%8 of Philox4x32-10 at counter (j/8, i, b*H + h, offset)
-        // under key (seed_lo, seed_hi) (draw t = bits 16*(t%2) of word t/2),
-        // and is kept when the draw is >= drop_thr. A lane holds keys
-        // 4g..4g+3 of the two 16-key blocks of chunk kc; lanes g and g^1 (the
-        // two 16-lane rows a v_permlane16_swap pairs) need the same two groups
-        // of 8 keys, g even the low four draws and g odd the high four. So
-        // each lane computes one group (g even that of the first block, g odd
-        // that of the second) and two swaps hand each lane the other lane's
-        // words it needs. Kept probabilities are scaled by 1/(1-p) in the
-        // epilogue.
-        auto drop_chunk = [&](int kc) __attribute__((always_inline)) {
-            uint32_t group = (uint32_t)((k0 + 32 * kc) >> 3) + 2u * (uint32_t)(g & 1) + (uint32_t)(g >> 1);
-            // Opaque to the optimiser: the counter grows linearly with the
-            // tile, and loop strength reduction otherwise keeps the first
-            // round's 64-bit product for every chunk position of a stage live
-            // across the scan (16 VGPRs), which spills.
-            asm volatile("" : "+v"(group));
+    // ---- dropout on P: zero the probabilities of dropped keys ----
+    // Key j of query row i (both within the sequence) of head (b, h) takes
+    // 16-bit draw j%8 of Philox4x32-10 at counter (j/8, i, b*H + h, offset)
+    // under key (seed_lo, seed_hi) (draw t = bits 16*(t%2) of word t/2),
+    // and is kept when the draw is >= drop_thr. A lane holds keys
+    // 4g..4g+3 of the two 16-key blocks of chunk kc; lanes g and g^1 (the
+    // two 16-lane rows a v_permlane16_swap pairs) need the same two groups
+    // of 8 keys, g even the low four draws and g odd the high four. So
+    // each lane computes one group (g even that of the first block, g odd
+    // that of the second) and two swaps hand each lane the other lane's
+    // words it needs. Kept probabilities are scaled by 1/(1-p) in the
+    // epilogue.
+    auto drop_chunk = [&](const int k0, PBT& pb, int kc) __attribute__((always_inline)) {
+        uint32_t group = (uint32_t)((k0 + 32 * kc) >> 3) + 2u * (uint32_t)(g & 1) + (uint32_t)(g >> 1);
+        // Opaque to the optimiser: the counter grows linearly with the
+        // tile, and loop strength reduction otherwise keeps the first
+        // round's 64-bit product for every chunk position of a stage live
+        // across the scan (16 VGPRs), which spills.
+        asm volatile("" : "+v"(group));
 #pragma unroll
-            for (int qb = 0; qb < QB; ++qb) {
-                const uint32_t qrow = (uint32_t)(qw0 + 16 * qb + l16);
-                const U32x4 r = philox4x32_10(group, qrow, (uint32_t)bh, a.offset, a.seed_lo, a.seed_hi);
-                // after the swaps: x = this lane's two words for the first
-                // block, y = for the second
-                const auto s0 = __builtin_amdgcn_permlane16_swap(r.w[0], r.w[2], false, false);
-                const auto s1 = __builtin_amdgcn_permlane16_swap(r.w[1], r.w[3], false, false);
-                const uint32_t w[4] = {s0[0], s1[0], s0[1], s1[1]};
-                // Keep mask per 16-bit half, 0xFFFF for draw >= drop_thr and 0
-                // otherwise, in three packed 16-bit integer ops per word:
-                // sat(thr - draw) is 0 exactly for kept keys, min(., 1) - 1
-                // (wrapping) maps 0 to 0xFFFF and 1 to 0. drop_thr <= 0xFFFF, and
-                // drop_thr = 0 keeps every key.
-                const uint32_t thr2 = a.drop_thr * 0x00010001u;
-                const uint32_t one2 = 0x00010001u;
-                uint32_t m[4];
+        for (int qb = 0; qb < QB; ++qb) {
+            const uint32_t qrow = (uint32_t)(qw0 + 16 * qb + l16);
+            const U32x4 r = philox4x32_10(group, qrow, (uint32_t)bh, a.offset, a.seed_lo, a.seed_hi);
+            // after the swaps: x = this lane's two words for the first
+            // block, y = for the second
+            const auto s0 = __builtin_amdgcn_permlane16_swap(r.w[0], r.w[2], false, false);
+            const auto s1 = __builtin_amdgcn_permlane16_swap(r.w[1], r.w[3], false, false);
+            const uint32_t w[4] = {s0[0], s1[0], s0[1], s1[1]};
+            // Keep mask per 16-bit half, 0xFFFF for draw >= drop_thr and 0
+            // otherwise, in three packed 16-bit integer ops per word:
+            // sat(thr - draw) is 0 exactly for kept keys, min(., 1) - 1
+            // (wrapping) maps 0 to 0xFFFF and 1 to 0. drop_thr <= 0xFFFF, and
+            // drop_thr = 0 keeps every key.
+            const uint32_t thr2 = a.drop_thr * 0x00010001u;
+            const uint32_t one2 = 0x00010001u;
+            uint32_t m[4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    uint32_t over, m01;
-                    asm("v_pk_sub_u16 %0, %1, %2 clamp" : "=v"(over) : "v"(thr2), "v"(w[e]));
-                    asm("v_pk_min_u16 %0, %1, %2" : "=v"(m01) : "v"(over), "v"(one2));
-                    asm("v_pk_sub_u16 %0, %1, %2" : "=v"(m[e]) : "v"(m01), "v"(one2));
-                }
-                typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
-                u32x4v bits = __builtin_bit_cast(u32x4v, pb[qb][kc]);
-                bits &= u32x4v{m[0], m[1], m[2], m[3]};
-                pb[qb][kc] = __builtin_bit_cast(half8, bits);
+            for (int e = 0; e < 4; ++e) {
+                uint32_t over, m01;
+                asm("v_pk_sub_u16 %0, %1, %2 clamp" : "=v"(over) : "v"(thr2), "v"(w[e]));
+                asm("v_pk_min_u16 %0, %1, %2" : "=v"(m01) : "v"(over), "v"(one2));
+                asm("v_pk_sub_u16 %0, %1, %2" : "=v"(m[e]) : "v"(m01), "v"(one2));
             }
-        };
+            typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+            u32x4v bits = __builtin_bit_cast(u32x4v, pb[qb][kc]);
+            bits &= u32x4v{m[0], m[1], m[2], m[3]};
+            pb[qb][kc] = __builtin_bit_cast(half8, bits);
+        }
+    };
 
-        // ---- O^T += V^T P^T on MFMA, for 32-key chunk kc ----
-        // Source lane l16 of group g points at row 4g + l16/4 (+16 for the second
-        // half) and columns 16*db + 4*(l16%4) .. +3; the transposing read returns
-        // V[32kc + 4g + e][16db + l16] in element e.
-        auto read_v = [&](int kc, int db) __attribute__((always_inline)) {
-            const char* p0 = ldsV + (rv ^ (db << 5)) + kc * 32 * D * 2;
-            const s16x4 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p0);
-            const s16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0 + 16 * D * 2));
-            const half4 h0 = __builtin_bit_cast(half4, t0);
-            const half4 h1 = __builtin_bit_cast(half4, t1);
-            return half8{h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
-        };
-        // At D=128 (2 waves per SIMD, registers to spare) the V fragments of the
-        // first chunk are read here, before the softmax, so that their LDS
-        // latency hides under its VALU work. At D=64 the registers are not there.
-        constexpr int VPRE = (D == 128) ? DB : 0;
-        half8 vpre[VPRE > 0 ? VPRE : 1];
+    // ---- O^T += V^T P^T on MFMA ----
+    // Source lane l16 of group g points at row 4g + l16/4 (+16 for the second
+    // half) and columns 16*db + 4*(l16%4) .. +3; the transposing read returns
+    // V[32kc + 4g + e][16db + l16] in element e.
+    auto read_v = [&](const char* const ldsV, uint32_t rv, int kc, int db) __attribute__((always_inline)) {
+        const char* p0 = ldsV + (rv ^ (db << 5)) + kc * 32 * D * 2;
+        const s16x4 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p0);
+        const s16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0 + 16 * D * 2));
+        const half4 h0 = __builtin_bit_cast(half4, t0);
+        const half4 h1 = __builtin_bit_cast(half4, t1);
+        return half8{h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
+    };
+    // At D=128 (2 waves per SIMD, registers to spare) the V fragments of the
+    // first chunk are read before the softmax, so that their LDS latency hides
+    // under its VALU work. At D=64 the registers are not there.
+    constexpr int VPRE = (D == 128) ? DB : 0;
+    typedef half8 VPreT[VPRE > 0 ? VPRE : 1];
+    auto pv_tile = [&](const char* const ldsV, uint32_t rv, const PBT& pb, const VPreT& vpre)
+                       __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < VPRE; ++i) vpre[i] = read_v(0, i);
-        auto pv_chunk = [&](int kc) __attribute__((always_inline)) {
+        for (int kc = 0; kc < NKC; ++kc)
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
-                const half8 va = (kc == 0 && db < VPRE) ? vpre[db] : read_v(kc, db);
+                const half8 va = (kc == 0 && db < VPRE) ? vpre[db] : read_v(ldsV, rv, kc, db);
 #pragma unroll
                 for (int qb = 0; qb < QB; ++qb)
                     oacc[db][qb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb[qb][kc], oacc[db][qb], 0, 0, 0);
             }
-        };
+    };
 
-        // Exponentiate the whole tile, then one check per tile.
-        float rs[QB];
-        auto exponentiate = [&]() __attribute__((always_inline)) {
+    // Exponentiate the whole tile against the current reference; rs gets the
+    // row sums used by the check and added to l.
+    auto exponentiate = [&](const SAccT& sacc, PBT& pb, float (&rs)[QB]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            rs[qb] = 0.f;
+#pragma unroll
+            for (int kc = 0; kc < NKC; ++kc) exp_chunk(sacc, pb, qb, kc, rs[qb]);
+        }
+        if (ROWSUM_MFMA) {
+            // the tile's full row sums on the matrix unit (each lane gets
+            // its query's sum over all BN keys): an MFMA with an all-ones
+            // A operand sums the B operand (P^T) over its 32 keys. At D=64
+            // the constant stays in registers for the whole scan; at D=128
+            // it is rebuilt here with volatile moves, which measured
+            // faster there than keeping it live.
+            half8 kOnes8 = kOnesKeep;
+            if (!KEEP_ONES) {
+                uint32_t one2[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) asm volatile("v_mov_b32 %0, 0x3c003c00" : "=v"(one2[i]));
+                typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+                kOnes8 = __builtin_bit_cast(half8, u32x4v{one2[0], one2[1], one2[2], one2[3]});
+            }
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb) {
-                rs[qb] = 0.f;
+                f32x4 ls = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int kc = 0; kc < NKC; ++kc) exp_chunk(qb, kc, rs[qb]);
+                for (int kc = 0; kc < NKC; ++kc)
+                    ls = __builtin_amdgcn_mfma_f32_16x16x32_f16(kOnes8, pb[qb][kc], ls, 0, 0, 0);
+                rs[qb] = ls[0];
             }
-            if (ROWSUM_MFMA) {
-                // the tile's full row sums on the matrix unit (each lane gets
-                // its query's sum over all BN keys): an MFMA with an all-ones
-                // A operand sums the B operand (P^T) over its 32 keys. At D=64
-                // the constant stays in registers for the whole scan; at D=128
-                // it is rebuilt here with volatile moves, which measured
-                // faster there than keeping it live.
-                half8 kOnes8 = kOnesKeep;
-                if (!KEEP_ONES) {
-                    uint32_t one2[4];
+        }
+    };
+    // True (on every lane) when a row sum of the speculative exponentiation
+    // reached 2^15, i.e. some p may have overflowed fp16.
+    auto overflowed = [&](const float (&rs)[QB]) __attribute__((always_inline)) {
+        bool over = false;
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) asm volatile("v_mov_b32 %0, 0x3c003c00" : "=v"(one2[i]));
-                    typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
-                    kOnes8 = __builtin_bit_cast(half8, u32x4v{one2[0], one2[1], one2[2], one2[3]});
-                }
+        for (int qb = 0; qb < QB; ++qb) over |= !(rs[qb] < kSpeculateLimit);
+        return __builtin_amdgcn_ballot_w64(over) != 0;  // wave-uniform
+    };
+    auto rebase = [&](const SAccT& sacc) __attribute__((always_inline)) {
 #pragma unroll
-                for (int qb = 0; qb < QB; ++qb) {
-                    f32x4 ls = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int qb = 0; qb < QB; ++qb) move_reference(qb, row_max(sacc, qb, 0, NKB));
+    };
+
+    // One compute tile: keys k0 .. k0+BN-1, K and V at the given LDS addresses.
+    auto compute_tile = [&](const int k0, const char* const ldsK, const char* const ldsV)
+                            __attribute__((always_inline)) {
+        uint32_t rv = rdV0;
+        asm volatile("" : "+v"(rv));
+        SAccT sacc;
+        scores(k0, ldsK, sacc);
+        VPreT vpre;
 #pragma unroll
-                    for (int kc = 0; kc < NKC; ++kc)
-                        ls = __builtin_amdgcn_mfma_f32_16x16x32_f16(kOnes8, pb[qb][kc], ls, 0, 0, 0);
-                    rs[qb] = ls[0];
-                }
-            }
-        };
+        for (int i = 0; i < VPRE; ++i) vpre[i] = read_v(ldsV, rv, 0, i);
+        PBT pb;
+        float rs[QB];
         bool move_ref = fresh;
         if (!move_ref) {
-            exponentiate();
-            bool over = false;
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb) over |= !(rs[qb] < kSpeculateLimit);
-            move_ref = __builtin_amdgcn_ballot_w64(over) != 0;  // wave-uniform
+            exponentiate(sacc, pb, rs);
+            move_ref = overflowed(rs);
         }
         if (move_ref) {
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb) move_reference(qb, row_max(qb, 0, NKB));
-            exponentiate();
+            rebase(sacc);
+            exponentiate(sacc, pb, rs);
         }
         fresh = false;
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) l_run[qb] += rs[qb];
         if (DROP) {
 #pragma unroll
-            for (int kc = 0; kc < NKC; ++kc) drop_chunk(kc);
+            for (int kc = 0; kc < NKC; ++kc) drop_chunk(k0, pb, kc);
         }
         if (FA2_SETPRIO) __builtin_amdgcn_s_setprio(FA2_PRIO_PV);
-#pragma unroll
-        for (int kc = 0; kc < NKC; ++kc) pv_chunk(kc);
+        pv_tile(ldsV, rv, pb, vpre);
         if (FA2_SETPRIO) __builtin_amdgcn_s_setprio(0);
     };
 
@@ -787,6 +807,8 @@ void fa2_fwd_kernel(KernelArgs a) {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
         if (t + 1 < t_end) issue_tile(t + 1, Int<1 - ST>{});
+        auto ldsK = [&](int j) { return reinterpret_cast<const char*>(smem) + 2 * ((ST * 2 + 0) * LTILE + j * TILE); };
+        auto ldsV = [&](int j) { return reinterpret_cast<const char*>(smem) + 2 * ((ST * 2 + 1) * LTILE + j * TILE); };
 #pragma unroll
         for (int j = 0; j < SUB; ++j) {
             const int k0 = t * KB + j * BN;
@@ -796,8 +818,7 @@ void fa2_fwd_kernel(KernelArgs a) {
                 if (k0 > qw0 + QW - 1 + a.wr) break;               // right of this wave's band
                 if (k0 + BN - 1 < qw0 - a.wl) continue;            // left of this wave's band
             }
-            compute_tile(k0, reinterpret_cast<const char*>(smem) + 2 * ((ST * 2 + 0) * LTILE + j * TILE),
-                         reinterpret_cast<const char*>(smem) + 2 * ((ST * 2 + 1) * LTILE + j * TILE));
+            compute_tile(k0, ldsK(j), ldsV(j));
         }
     };
 
