@@ -768,6 +768,7 @@ void fa2_fwd_kernel(KernelArgs a) {
     // One compute tile: keys k0 .. k0+BN-1, K and V at the given LDS addresses.
     auto compute_tile = [&](const int k0, const char* const ldsK, const char* const ldsV)
                             __attribute__((always_inline)) {
+        // the per-column-block V offsets, derived inside the tile like the K ones
         uint32_t rv = rdV0;
         asm volatile("" : "+v"(rv));
         SAccT sacc;
