@@ -1050,14 +1050,25 @@ uint32_t drop_threshold(float p) {
     return t >= 65535.0 ? 0xFFFFu : (uint32_t)t;
 }
 
+// Packed causal batches take the half-height workgroups when their sequences
+// are short on average (total rows / sequences below the dense threshold):
+// 24 packed sequences of 64 to 4096 rows ran 5.5 % faster that way. (Windowed
+// launches keep the full height: 3.5-4.6 % slower with half height at
+// S = 8192, windows (1024, 1024) and (1024, 0).)
+template <class SH>
+bool packed_half_height(const LaunchArgs& a) {
+    return FA2_SMALL_CAUSAL && (long long)a.total <= (long long)a.B * (SH::D == 64 ? kShortCausal64 : kShortCausal128);
+}
+
 hipError_t launch_forward(const LaunchArgs& a, hipStream_t stream) {
     const long long units = (long long)a.B * a.H;
-    const bool small = !a.cu_seqlens && causal_window(a.S, a.window_left, a.window_right);
-    if (a.D == 64)
-        return (small && causal_half_height<Shape64>(units, a.S)) ? launch_d<Shape64c>(a, stream)
-                                                                   : launch_d<Shape64>(a, stream);
-    return (small && causal_half_height<Shape128>(units, a.S)) ? launch_d<Shape128c>(a, stream)
-                                                               : launch_d<Shape128>(a, stream);
+    const bool causal = causal_window(a.S, a.window_left, a.window_right);
+    if (a.D == 64) {
+        const bool half = causal && (a.cu_seqlens ? packed_half_height<Shape64>(a) : causal_half_height<Shape64>(units, a.S));
+        return half ? launch_d<Shape64c>(a, stream) : launch_d<Shape64>(a, stream);
+    }
+    const bool half = causal && (a.cu_seqlens ? packed_half_height<Shape128>(a) : causal_half_height<Shape128>(units, a.S));
+    return half ? launch_d<Shape128c>(a, stream) : launch_d<Shape128>(a, stream);
 }
 
 }  // namespace fa2
