@@ -218,8 +218,9 @@ def test_kernel_config():
 def test_kernel_config_shapes():
     """Causal grids that fit in one round of resident workgroups (2 per CU at
     D=64, 1 at D=128, 256 CUs), or whose sequences are short (S < 4096 at
-    D=64, S <= 1024 at D=128), use half-height workgroups; other causal grids,
-    and every non-causal grid, the full height."""
+    D=64, S <= 1024 at D=128), use half-height workgroups, and so do unmasked
+    grids whose full-height grid is smaller than one round; other grids use the
+    full height."""
     full64 = fa2.fa2_kernel_config(4, 8, 4096, 64, 0)
     assert (full64["rows_per_block"], full64["threads_per_block"], full64["blocks"]) == (256, 512, 512)
     half64 = fa2.fa2_kernel_config(4, 8, 4096, 64, 1)      # 512 full-height blocks: one round
@@ -237,6 +238,11 @@ def test_kernel_config_shapes():
     assert fa2.fa2_kernel_config(2, 32, 4096, 64, 1)["rows_per_block"] == 256    # 1024 blocks, S not short
     assert fa2.fa2_kernel_config(8, 16, 1024, 128, 1)["rows_per_block"] == 128
     assert fa2.fa2_kernel_config(8, 16, 1025, 128, 1)["rows_per_block"] == 256
+    # unmasked grids smaller than one round of full-height workgroups: half height
+    assert fa2.fa2_kernel_config(1, 8, 4096, 64, 0)["rows_per_block"] == 128     # 128 < 512 full-height blocks
+    assert fa2.fa2_kernel_config(3, 8, 4096, 64, 0)["rows_per_block"] == 128     # 384 < 512
+    assert fa2.fa2_kernel_config(1, 8, 4096, 128, 0)["rows_per_block"] == 128    # 128 < 256
+    assert fa2.fa2_kernel_config(1, 16, 4096, 128, 0)["rows_per_block"] == 256   # 256: one round
 
 
 def test_forward_rejects_bad_tensors():
