@@ -925,11 +925,12 @@ bool causal_half_height(long long units, int S) {
     return fits_one_round<SH>(units, S) ||
            (FA2_SMALL_CAUSAL && S <= (SH::D == 64 ? kShortCausal64 : kShortCausal128));
 }
-// Unmasked dense launches whose full-height grid is smaller than one round of
-// resident workgroups leave compute units short of work: half the height
-// doubles the workgroups. Measured on one GPU: +24-25 % at 64-128 full-height
-// workgroups and +8 % at 384 (D = 64), +19 % at 128 (D = 128), even at 256
-// (D = 64), and 3.5-6 % slower once the full-height grid fills a round.
+// Other dense launches (unmasked or windowed) whose full-height grid is
+// smaller than one round of resident workgroups leave compute units short of
+// work: half the height doubles the workgroups. Measured on one GPU, unmasked:
+// +24-25 % at 64-128 full-height workgroups and +8 % at 384 (D = 64), +19 % at
+// 128 (D = 128), even at 256 (D = 64), and 3.5-6 % slower once the full-height
+// grid fills a round; windowed grids of 256 full-height workgroups +2-5 %.
 template <class SH>
 bool plain_half_height(long long units, int S) {
     return FA2_SMALL_CAUSAL && units * ((S + SH::BM - 1) / SH::BM) < (long long)kCUs * wg_per_cu<SH>();
@@ -1047,14 +1048,10 @@ TileShape tile_shape(int D) { return D == 128 ? describe<Shape128>() : describe<
 // right side is 0 (the rule launch_d applies).
 static bool causal_window(int S, int wl, int wr) { return (wl < 0 || wl >= S) && wr == 0; }
 
-// Neither side of the window bounds the keys: the unmasked kernel.
-static bool open_window(int S, int wl, int wr) { return (wl < 0 || wl >= S) && (wr < 0 || wr >= S); }
-
 // Whether a dense launch runs the half-height workgroups.
 template <class SH>
 bool dense_half_height(long long units, int S, int wl, int wr) {
-    if (causal_window(S, wl, wr)) return causal_half_height<SH>(units, S);
-    return open_window(S, wl, wr) && plain_half_height<SH>(units, S);
+    return causal_window(S, wl, wr) ? causal_half_height<SH>(units, S) : plain_half_height<SH>(units, S);
 }
 
 TileShape dense_tile_shape(int D, long long units, int S, int window_left, int window_right) {
@@ -1073,8 +1070,8 @@ uint32_t drop_threshold(float p) {
 // Packed causal batches take the half-height workgroups when their sequences
 // are short on average (total rows / sequences below the dense threshold):
 // 24 packed sequences of 64 to 4096 rows ran 5.5 % faster that way. (Windowed
-// launches keep the full height: 3.5-4.6 % slower with half height at
-// S = 8192, windows (1024, 1024) and (1024, 0).)
+// grids of a round or more keep the full height: 3.5-4.6 % slower with half
+// height at B4 H8 S8192, windows (1024, 1024) and (1024, 0).)
 template <class SH>
 bool packed_half_height(const LaunchArgs& a) {
     return FA2_SMALL_CAUSAL && (long long)a.total <= (long long)a.B * (SH::D == 64 ? kShortCausal64 : kShortCausal128);
