@@ -31,7 +31,7 @@ LIB_PATH = os.path.join(_PKG, "libfa2.so")
 FA2_OK = 0
 STATUS_NAMES = {
     0: "FA2_OK", 1: "FA2_ERR_NULLPTR", 2: "FA2_ERR_SHAPE", 3: "FA2_ERR_SCALE", 4: "FA2_ERR_ALIGN",
-    5: "FA2_ERR_OVERFLOW", 6: "FA2_ERR_ALIAS", 7: "FA2_ERR_DEVICE", 8: "FA2_ERR_LAUNCH",
+    5: "FA2_ERR_OVERFLOW", 6: "FA2_ERR_DEVICE", 7: "FA2_ERR_LAUNCH", 8: "FA2_ERR_ALIAS",
     9: "FA2_ERR_ARG",
 }
 EXPORTED = ("fa2_fwd", "fa2_fwd_ex", "fa2_fwd_varlen", "fa2_strerror", "fa2_kernel_config")

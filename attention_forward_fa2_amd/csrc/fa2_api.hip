@@ -26,11 +26,13 @@ bool misaligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u)
 // Limits of the kernel's index arithmetic: row and key indices are 32-bit and
 // so is a row index plus a window side (each below 2^29 plus one tile), a
 // workgroup id is 31-bit, and a lane's byte offset into one K/V ring stage (up
-// to 64 rows of the row stride) is 32-bit.
+// to 64 rows of the row stride) is 32-bit. The grid is bounded with the
+// smallest workgroup height any shape has, so the limit holds for whichever
+// shape the launch picks.
 int overflow_status(long long units, int S, long long row_stride_kv, int D) {
     if (S >= (1 << 29)) return FA2_ERR_OVERFLOW;
-    const fa2::TileShape ts = fa2::tile_shape(D);
-    const long long blocks = units * ((S + ts.rows_per_block - 1) / ts.rows_per_block);
+    const long long rows = fa2::min_rows_per_block(D);
+    const long long blocks = units * ((S + rows - 1) / rows);
     if (units > 0x7fffffffll || blocks > 0x7fffffffll) return FA2_ERR_OVERFLOW;
     if (row_stride_kv * 2 * 64 >= (1ll << 32)) return FA2_ERR_OVERFLOW;
     return FA2_OK;
@@ -97,10 +99,12 @@ int validate_varlen(const void* q, const void* k, const void* v, const void* o, 
     if ((st = overflow_status((long long)num_seqs * H, max_seqlen, (long long)H_kv * D, D)) != FA2_OK) return st;
     if ((long long)H * D >= (1ll << 31)) return FA2_ERR_OVERFLOW;
     {
-        // the packed grid rounds the (sequence, K/V head) units up to a multiple of 8
-        const fa2::TileShape ts = fa2::tile_shape(D);
+        // the packed grid rounds the (sequence, K/V head) units up to a multiple
+        // of 8; bounded with the smallest workgroup height (packed causal
+        // batches of short sequences take the half-height shape)
+        const long long rows = fa2::min_rows_per_block(D);
         const long long units8 = ((long long)num_seqs * H_kv + 7) / 8 * 8;
-        const long long nqt = (max_seqlen + ts.rows_per_block - 1) / ts.rows_per_block;
+        const long long nqt = (max_seqlen + rows - 1) / rows;
         if (units8 * nqt * (H / H_kv) > 0x7fffffffll) return FA2_ERR_OVERFLOW;
     }
     const size_t nq = (size_t)total * H * D * 2, nkv = (size_t)total * H_kv * D * 2, nl = (size_t)total * H * 4;
@@ -175,7 +179,7 @@ extern "C" const char* fa2_strerror(int status) {
         case FA2_ERR_OVERFLOW:
             return "the sequence length must be < 2^29 and the grid must fit in 2^31-1 workgroups";
         case FA2_ERR_ALIAS: return "o or lse overlaps an input or each other";
-        case FA2_ERR_DEVICE: return "the current HIP device is not a gfx950 GPU";
+        case FA2_ERR_DEVICE: return "there is no current HIP device, or it is not a gfx950 GPU";
         case FA2_ERR_LAUNCH: return "the kernel launch failed";
         case FA2_ERR_ARG: return "window sizes must be >= -1 and the dropout probability in [0, 1)";
         default: return "unknown status";

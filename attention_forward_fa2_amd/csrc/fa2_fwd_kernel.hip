@@ -146,7 +146,8 @@ __device__ __forceinline__ float sum_xor32(float x) {
 // later LDS read of the other ring stage wait for them, which removes the
 // overlap of the next tile's load with this tile's math. The kernel waits for
 // them itself (vmcnt(0)) before the barrier that publishes a stage. M0 carries
-// the LDS base; nothing else in this kernel uses M0.
+// the LDS base; it is an input operand of the asm ("{m0}"), so the compiler sets
+// it and knows its value wherever else M0 may be needed.
 //   dma_16B_s: address = 64-bit wave-uniform base (SGPRs) + 32-bit lane offset.
 //   dma_16B_v: full 64-bit per-lane address.
 __device__ __forceinline__ void dma_16B_s(const void* sbase_in, uint32_t voff, uint32_t lds_base) {
@@ -158,21 +159,20 @@ __device__ __forceinline__ void dma_16B_s(const void* sbase_in, uint32_t voff, u
     const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
     const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
     const void* sbase = reinterpret_cast<const void*>((hi << 32) | lo);
+    // s_nop: one wait state between the write of M0 and the load that reads it
     asm volatile(
-        "s_mov_b32 m0, %2\n\t"
         "s_nop 0\n\t"
         "global_load_lds_dwordx4 %0, %1"
         :
-        : "v"(voff), "s"(sbase), "s"(lds_base)
+        : "v"(voff), "s"(sbase), "{m0}"(lds_base)
         : "memory");
 }
 __device__ __forceinline__ void dma_16B_v(const void* src, uint32_t lds_base) {
     asm volatile(
-        "s_mov_b32 m0, %1\n\t"
         "s_nop 0\n\t"
         "global_load_lds_dwordx4 %0, off"
         :
-        : "v"(src), "s"(lds_base)
+        : "v"(src), "{m0}"(lds_base)
         : "memory");
 }
 
@@ -363,6 +363,16 @@ __device__ __forceinline__ U32x4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_
 #define FA2_MFMA_ROWSUM 2
 #endif
 
+// Debug build (FA2_POISON_LDS=1, a separate library): before each ring stage
+// is refilled, every lane overwrites the LDS chunks its own direct-to-LDS loads
+// are about to fill with NaN (all bits set) and waits for those writes. A read
+// that the wait/barrier protocol fails to order after the loads, or after the
+// last reads of the stage's previous tile, then sees NaN, which reaches the
+// output. With a correct protocol the outputs are those of the normal build.
+#ifndef FA2_POISON_LDS
+#define FA2_POISON_LDS 0
+#endif
+
 // Occupancy target of the dropout instances at D=64 (waves per SIMD); the
 // generator's registers do not fit the 4-wave budget without spills.
 #ifndef FA2_DROP_WAVES
@@ -443,6 +453,18 @@ void fa2_fwd_kernel(KernelArgs a) {
     auto issue_tile = [&](int t, auto st_c) {
         constexpr int ST = decltype(st_c)::value;
         const int k0 = t * KB;
+        if (FA2_POISON_LDS) {
+            typedef uint32_t u32x4p __attribute__((ext_vector_type(4)));
+            typedef __attribute__((address_space(3))) u32x4p lds_u32x4;
+#pragma unroll
+            for (int i = 0; i < LOADS; ++i) {
+                const uint32_t dst = lds_base + 2u * (i * NW + wave) * 512 + 16u * lane;
+                const u32x4p nan4 = u32x4p{~0u, ~0u, ~0u, ~0u};
+                *(lds_u32x4*)(uintptr_t)(dst + 2u * (ST * 2 + 0) * LTILE) = nan4;
+                *(lds_u32x4*)(uintptr_t)(dst + 2u * (ST * 2 + 1) * LTILE) = nan4;
+            }
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        }
         if (k0 + KB <= len) {
 #pragma unroll
             for (int i = 0; i < LOADS; ++i) {
@@ -959,9 +981,12 @@ hipError_t launch_shape(const LaunchArgs& a, const KernelArgs& k, hipStream_t st
     constexpr unsigned kMaxX = 1u << 22;
     const unsigned nb = (unsigned)k.nblocks;
     const dim3 grid(nb <= kMaxX ? nb : kMaxX, nb <= kMaxX ? 1u : (nb + kMaxX - 1) / kMaxX);
-    hipLaunchKernelGGL(kern, grid, dim3(SH::THREADS), SH::LDS_BYTES, stream, k);
+    // hipLaunchKernel returns this launch's own status (an error left behind by
+    // an earlier, unrelated runtime call of the caller is not reported as ours).
+    KernelArgs karg = k;
+    void* params[] = {&karg};
     (void)a;
-    return hipGetLastError();
+    return hipLaunchKernel((const void*)kern, grid, dim3(SH::THREADS), params, SH::LDS_BYTES, stream);
 }
 
 template <class SH>
@@ -1002,7 +1027,11 @@ hipError_t launch_d(const LaunchArgs& a, hipStream_t stream) {
     k.BH = a.B * a.H;
     k.BHkv = a.B * a.H_kv;
     k.nqt = (a.S + SH::BM - 1) / SH::BM;
-    k.nblocks = a.cu_seqlens ? ((k.BHkv + 7) / 8) * 8 * k.nqt * k.group : k.BH * k.nqt;
+    // in 64-bit: the argument checks bound it by 2^31 - 1 for every shape
+    const long long nblocks = a.cu_seqlens ? (((long long)k.BHkv + 7) / 8) * 8 * k.nqt * k.group
+                                           : (long long)k.BH * k.nqt;
+    if (nblocks > 0x7fffffffll) return hipErrorInvalidConfiguration;
+    k.nblocks = (int)nblocks;
     k.c = (float)((double)a.scale * kLog2e);
     // A dense grid that is resident in one round takes the serpentine causal order.
     k.serp = (!a.cu_seqlens && k.nblocks <= kCUs * wg_per_cu<SH>()) ? kCUs / 8 : 0;
@@ -1043,6 +1072,11 @@ TileShape describe() {
 }
 
 TileShape tile_shape(int D) { return D == 128 ? describe<Shape128>() : describe<Shape64>(); }
+
+int min_rows_per_block(int D) {
+    return D == 128 ? (Shape128::BM < Shape128c::BM ? Shape128::BM : Shape128c::BM)
+                    : (Shape64::BM < Shape64c::BM ? Shape64::BM : Shape64c::BM);
+}
 
 // A dense launch is causal when the left side of the window is open and the
 // right side is 0 (the rule launch_d applies).

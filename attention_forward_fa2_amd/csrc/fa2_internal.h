@@ -13,10 +13,13 @@ struct TileShape {
     int lds_bytes;        // dynamic LDS per workgroup
 };
 
-// The full-height shape for head dimension D (64 or 128); every other shape
-// has fewer rows per workgroup only when the full-height grid is small, so
-// this one bounds the grid size.
+// The full-height shape for head dimension D (64 or 128).
 TileShape tile_shape(int D);
+
+// The fewest query rows per workgroup of any shape a launch at head dimension
+// D may pick (the half-height shapes). Grid-size limits are checked with it, so
+// they hold whichever shape the launch selects.
+int min_rows_per_block(int D);
 
 // The shape a dense launch of `units` (batch*head) heads of length S uses.
 TileShape dense_tile_shape(int D, long long units, int S, int window_left, int window_right);

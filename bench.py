@@ -17,7 +17,8 @@ Prints one JSON line:
                median and range over R replays (the pages' own timing method;
                a cross-check, not the value)
 
-    python bench.py [--gpus 1] [--steps 200] [--warmup 200] [--workload 2] [--causal] [--graph 100]
+    python bench.py [--gpus 1] [--steps 200] [--warmup 200] [--settle-ms 500] [--workload 2] [--causal]
+                    [--graph 100]
     python bench.py --feature {gqa,mqa,window,varlen,dropout} [--causal]
 
 --feature times one of the production-feature workloads (GQA/MQA, local
@@ -223,6 +224,9 @@ def main():
     ap.add_argument("--causal", action="store_true", help="run the causal variant of the workload")
     ap.add_argument("--feature", choices=["gqa", "mqa", "window", "varlen", "dropout"], default=None,
                     help="time a production-feature workload instead of a plain one")
+    ap.add_argument("--settle-ms", type=float, default=500.0,
+                    help="untimed launches for at least this long before the warmup steps, so the GPU clock "
+                         "has ramped up (reported as clock_settle in the line); 0 disables")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cold", action="store_true",
                     help="write a 512 MiB buffer between launches so inputs come from HBM, not L2/MALL; "
@@ -295,10 +299,24 @@ def main():
         cfg = {"B": w.B, "H": w.H, "S": w.S, "D": w.D, "causal": causal, "scale": w.scale,
                "inputs": "fp16 iid normal, seeds 1000*w+{0,1,2}"}
 
+    # Clock settling: the GPU's clock needs on the order of 100 back-to-back
+    # launches (about 20-50 ms of this kernel) to ramp up, and steps timed
+    # before that run 5-20 % slow whatever --warmup says. So before the W
+    # warmup steps, launches run (untimed, reported in the line) until at
+    # least --settle-ms of GPU time has passed.
+    settle = {"launches": 0, "ms": 0.0}
+    if args.settle_ms > 0:
+        s0 = time.perf_counter()
+        while (time.perf_counter() - s0) * 1e3 < args.settle_ms and settle["launches"] < 20000:
+            for _ in range(10):
+                step()
+            torch.cuda.synchronize()
+            settle["launches"] += 10
+        settle["ms"] = round((time.perf_counter() - s0) * 1e3, 1)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    log("bench: warmup done")
+    log(f"bench: clock settling {settle['launches']} launches ({settle['ms']} ms), warmup {args.warmup} done")
 
     # Two timed passes of the same K steps on the launch stream. The first has
     # only the outer pair of events and gives the step time (value); the second
@@ -410,6 +428,8 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "graph_timing": graph_timing,
+        "clock_settle": {"launches": settle["launches"], "ms": settle["ms"],
+                         "note": "untimed launches of the same step before the warmup steps"},
     }
     print(json.dumps(rec), flush=True)
 

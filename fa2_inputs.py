@@ -81,20 +81,6 @@ def make_random(seed: int, B: int, H: int, S: int, D: int, sigma_qk: float = 1.0
             normal_f16(seed + 2, shape, sigma_v))
 
 
-def sample_rows(cid: int, n: int, seed: int = 7) -> np.ndarray:
-    """Flat row indices (b*H+h)*S+i for sampled checks: the first and last row
-    of every head's first and last query block plus ``n`` uniform picks."""
-    w = WORKLOADS[cid]
-    g = np.random.Generator(np.random.PCG64(seed + 31 * cid))
-    heads = w.B * w.H
-    fixed = []
-    for hd in (0, heads - 1):
-        for i in (0, 1, w.S - 2, w.S - 1):
-            fixed.append(hd * w.S + i)
-    picks = g.integers(0, heads * w.S, size=n)
-    return np.unique(np.concatenate([np.array(fixed, dtype=np.int64), picks.astype(np.int64)]))
-
-
 # ---- workloads of the production features (GQA/MQA, local window, packed
 # variable-length sequences, dropout). The page lists these features without
 # measuring them; the shapes below keep the head dimension and value

@@ -43,6 +43,10 @@
  *
  * Precision: fp16 inputs, fp32 accumulation (MFMA), fp32 softmax state, fp16
  * output rounded to nearest even, fp32 LSE.
+ *
+ * Inputs must be finite. With an infinity or NaN among q, k or v the call still
+ * completes and writes every output, but the values are unspecified (the
+ * kernel's max and overflow tests assume finite scores).
  */
 #ifndef FA2_H
 #define FA2_H
@@ -51,10 +55,13 @@
 extern "C" {
 #endif
 
-/* Return codes. Argument checks run in this order before any HIP call, so
- * every code except FA2_ERR_DEVICE and FA2_ERR_LAUNCH is reported without
- * touching a GPU. FA2_ERR_ARG is checked after FA2_ERR_SCALE and before
- * FA2_ERR_ALIGN. */
+/* Return codes. Codes 0-7 are the plain entry point's; FA2_ERR_ALIAS and
+ * FA2_ERR_ARG were added after them for the aliasing check and the arguments
+ * of the extended entry points, so the first eight keep their values.
+ * Argument checks run in this order before any HIP call:
+ *   NULLPTR, SHAPE, SCALE, ARG, ALIGN, OVERFLOW, ALIAS,
+ * so every code except FA2_ERR_DEVICE and FA2_ERR_LAUNCH is reported without
+ * touching a GPU; the device check (DEVICE) and the launch (LAUNCH) follow. */
 typedef enum {
     FA2_OK = 0,
     FA2_ERR_NULLPTR = 1,   /* a tensor pointer (or cu_seqlens) is NULL                     */
@@ -62,11 +69,12 @@ typedef enum {
                               causal not 0 or 1                                            */
     FA2_ERR_SCALE = 3,     /* scale is not finite or not > 0                                */
     FA2_ERR_ALIGN = 4,     /* q, k, v or o not 16-byte aligned; lse or cu_seqlens not 4-byte */
-    FA2_ERR_OVERFLOW = 5,  /* sequence length >= 2^29, more than 2^31-1 workgroups, or a
-                              packed K/V row stride (H_kv*D) too large for 32-bit offsets    */
-    FA2_ERR_ALIAS = 6,     /* o or lse overlaps q, k, v (or cu_seqlens), or each other      */
-    FA2_ERR_DEVICE = 7,    /* the current HIP device is not a gfx950 GPU                    */
-    FA2_ERR_LAUNCH = 8,    /* the kernel launch failed (hipGetLastError)                    */
+    FA2_ERR_OVERFLOW = 5,  /* sequence length >= 2^29, more than 2^31-1 workgroups (counted
+                              at the smallest workgroup height, 128 query rows), or a packed
+                              K/V row stride (H_kv*D) too large for 32-bit offsets          */
+    FA2_ERR_DEVICE = 6,    /* no current HIP device, or it is not a gfx950 GPU            */
+    FA2_ERR_LAUNCH = 7,    /* the kernel launch failed (the status hipLaunchKernel returned) */
+    FA2_ERR_ALIAS = 8,     /* o or lse overlaps q, k, v (or cu_seqlens), or each other      */
     FA2_ERR_ARG = 9        /* a window side < -1, or dropout_p not in [0, 1)                */
 } fa2_status;
 

@@ -93,16 +93,17 @@ def test_misaligned(field, off):
 # Calls below always carry one error that is checked last (o aliasing q), so
 # reaching FA2_ERR_ALIAS shows every earlier check passed, and no call here can
 # ever reach a kernel launch with these fake pointers.
+ALIAS, DEVICE, ARG = 8, 6, 9
 
 def test_lse_needs_only_4_byte_alignment():
-    assert call(lse=L + 4, o=Q) == 6
+    assert call(lse=L + 4, o=Q) == ALIAS
 
 
 def test_overflow():
     assert call(S=1 << 29, D=64) == 5          # row index plus a window side must stay below 2^31
-    assert call(S=(1 << 29) - 1, D=128, o=Q) == 6
+    assert call(S=(1 << 29) - 1, D=128, o=Q) == ALIAS
     # tensors far beyond 2^31 elements are fine (64-bit addressing) ...
-    assert call(B=64, H=64, S=1 << 20, D=128, o=Q) == 6
+    assert call(B=64, H=64, S=1 << 20, D=128, o=Q) == ALIAS
     # ... but the grid must fit in 2^31 - 1 workgroups
     assert call(B=1 << 16, H=1 << 12, S=1 << 12, D=64) == 5
 
@@ -110,14 +111,14 @@ def test_overflow():
 def test_valid_arguments_reach_the_alias_check():
     for D in (64, 128):
         for causal in (0, 1):
-            assert call(D=D, causal=causal, o=Q) == 6
+            assert call(D=D, causal=causal, o=Q) == ALIAS
 
 
 def test_alias():
-    assert call(o=Q) == 6
-    assert call(lse=V + 100 * 64 * 2 // 2 * 2) == 6  # inside v
-    assert call(o=K + 16) == 6
-    assert call(lse=O + 64) == 6
+    assert call(o=Q) == ALIAS
+    assert call(lse=V + 100 * 64 * 2 // 2 * 2) == ALIAS  # inside v
+    assert call(o=K + 16) == ALIAS
+    assert call(lse=O + 64) == ALIAS
 
 
 def test_error_order():
@@ -170,37 +171,69 @@ def test_varlen_bad_shape(kw):
 @pytest.mark.parametrize("kw", [dict(wl=-2), dict(wr=-5), dict(p=-0.1), dict(p=1.0), dict(p=1.5),
                                 dict(p=float("nan")), dict(p=float("inf"))])
 def test_bad_window_or_dropout(kw):
-    assert call_ex(**kw) == 9
-    assert call_varlen(**kw) == 9
+    assert call_ex(**kw) == ARG
+    assert call_varlen(**kw) == ARG
 
 
 def test_ex_and_varlen_accept_valid_extras():
     # every call here also aliases o with q, the last check
     for kw in (dict(wl=0, wr=0), dict(wl=5, wr=-1), dict(wl=-1, wr=0), dict(p=0.0), dict(p=0.999, seed=2**64 - 1),
                dict(H=8, H_kv=1), dict(H=8, H_kv=8), dict(offset=2**32 - 1)):
-        assert call_ex(o=Q, **kw) == 6
-        assert call_varlen(o=Q, **kw) == 6
+        assert call_ex(o=Q, **kw) == ALIAS
+        assert call_varlen(o=Q, **kw) == ALIAS
 
 
 def test_varlen_alignment_and_alias():
     assert call_varlen(cu=CU + 2) == 4
-    assert call_varlen(cu=CU + 4, o=Q) == 6     # 4-byte alignment is enough
-    assert call_varlen(cu=O + 64) == 6          # the table inside o
-    assert call_varlen(lse=CU) == 6
+    assert call_varlen(cu=CU + 4, o=Q) == ALIAS     # 4-byte alignment is enough
+    assert call_varlen(cu=O + 64) == ALIAS          # the table inside o
+    assert call_varlen(lse=CU) == ALIAS
 
 
 def test_varlen_overflow():
     assert call_varlen(max_seqlen=1 << 29) == 5
     assert call_varlen(H=1 << 19, H_kv=1 << 19, D=64) == 5   # a K/V row stride too large for 32-bit lane offsets
-    assert call_varlen(H=1 << 10, H_kv=1 << 10, D=128, o=Q) == 6
+    assert call_varlen(H=1 << 10, H_kv=1 << 10, D=128, o=Q) == ALIAS
 
 
 def test_extended_error_order():
     # scale beats window/dropout beats alignment
     assert call_ex(scale=0.0, p=2.0, q=Q + 2) == 3
-    assert call_ex(p=2.0, q=Q + 2) == 9
-    assert call_varlen(wl=-3, cu=CU + 1) == 9
+    assert call_ex(p=2.0, q=Q + 2) == ARG
+    assert call_varlen(wl=-3, cu=CU + 1) == ARG
     assert call_ex(H_kv=3, p=2.0) == 2
+
+
+def test_status_codes_follow_the_boundary_table():
+    """The eight codes of the plain entry point keep their documented values;
+    the two added for the extended entry points come after them."""
+    assert fa2.STATUS_NAMES == {0: "FA2_OK", 1: "FA2_ERR_NULLPTR", 2: "FA2_ERR_SHAPE", 3: "FA2_ERR_SCALE",
+                                4: "FA2_ERR_ALIGN", 5: "FA2_ERR_OVERFLOW", 6: "FA2_ERR_DEVICE",
+                                7: "FA2_ERR_LAUNCH", 8: "FA2_ERR_ALIAS", 9: "FA2_ERR_ARG"}
+
+
+def test_valid_arguments_without_a_gpu_report_device():
+    """Arguments that pass every check reach the device check, which fails
+    here (no HIP device): FA2_ERR_DEVICE, and nothing is launched."""
+    assert call() == DEVICE
+    assert call(D=128, causal=1) == DEVICE
+    assert call_ex(wl=16, wr=0, p=0.25, seed=3) == DEVICE
+    assert call_varlen() == DEVICE
+    assert call_varlen(H=8, H_kv=2, D=64, wl=-1, wr=0) == DEVICE
+
+
+def test_grid_bound_counts_half_height_workgroups():
+    """Launches that pick the half-height (128-row) workgroups have twice the
+    workgroups of the full-height shape; the grid limit is checked at that
+    height. One packed sequence of one row with max_seqlen 2^29 - 1 and 127
+    query heads per K/V head: 8 units x 2^22 tiles x 127 heads > 2^31 - 1."""
+    assert call_varlen(nseq=1, total=1, max_seqlen=(1 << 29) - 1, H=127, H_kv=1, D=64, wl=-1, wr=0) == 5
+    assert call_varlen(nseq=1, total=1, max_seqlen=(1 << 29) - 1, H=127, H_kv=1, D=64) == 5
+    assert call_varlen(nseq=1, total=1, max_seqlen=(1 << 29) - 1, H=63, H_kv=1, D=64, wl=-1, wr=0, o=Q) == ALIAS
+    # dense short causal sequences (half height): 3 * 2^25 heads of 4095 rows
+    # are 3 * 2^29 workgroups at full height (below 2^31) but 3 * 2^30 at half
+    assert call(B=3, H=1 << 25, S=4095, D=64, causal=1) == 5
+    assert call(B=1, H=1 << 25, S=4095, D=64, causal=1, o=Q) == ALIAS
 
 
 def test_kernel_config():

@@ -1,6 +1,7 @@
 """Graph capture as the very first use of the library (GPU). In a fresh
 process, the first D = 128 full-height launch (which opts the kernel in to more
-than 64 KiB of LDS on its first call on a device) and the first D = 64 launch
+than 64 KiB of LDS on its first call on a device; the case is checked to use
+more than 64 KiB) and the first D = 64 launch
 are made inside a HIP graph capture; the replays must equal eager launches made
 afterwards, bit for bit."""
 import os
@@ -21,7 +22,11 @@ import attention_forward_fa2_amd as fa2
 from fa2_inputs import make_random
 
 dev = torch.device("cuda:0")
-cases = [(make_random(49_000, 2, 8, 2048, 128), False), (make_random(49_100, 1, 4, 700, 64), True)]
+# B1 H16 S4096 D128 non-causal is one round of 256 full-height workgroups,
+# whose 128 KiB of LDS needs the opt-in; the D = 64 case is causal.
+cfg = fa2.fa2_kernel_config(1, 16, 4096, 128, 0)
+assert cfg["rows_per_block"] == 256 and cfg["lds_bytes"] > 65536, cfg
+cases = [(make_random(49_000, 1, 16, 4096, 128), False), (make_random(49_100, 1, 4, 700, 64), True)]
 bufs = []
 for (q, k, v), causal in cases:
     t = [torch.from_numpy(x).to(dev) for x in (q, k, v)]

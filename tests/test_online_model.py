@@ -40,3 +40,107 @@ def test_skipping_the_rescale_breaks_it():
         o = o + p @ vd[k0:k0 + 16]          # the rescale of the old output is skipped
         m = m_new
     assert np.max(np.abs(o / l[:, None] - O[0, 0])) > 1e-3
+
+
+# ---- the kernel's lazy reference (oracle.online_model.lazy_reference_attention) ----
+
+from oracle.online_model import lazy_reference_attention  # noqa: E402
+
+
+def _ramp(direction, S=515, D=64, H=2, seed=902):
+    """Scores that rise (or fall) by about 180 base-2 units per 64 keys at
+    scale 1: rising keys raise every row's maximum on every tile, falling ones
+    never after the first."""
+    q = np.zeros((1, H, S, D), np.float16)
+    k = np.zeros((1, H, S, D), np.float16)
+    q[..., 0] = 4.0
+    ramp = (np.arange(S) * 0.5).astype(np.float16)
+    k[0, :, :, 0] = ramp if direction == "rising" else ramp[::-1]
+    _, _, v = make_random(seed, 1, H, S, D)
+    return q, k, v
+
+
+def _cases():
+    yield "sigma3", make_random(903, 1, 2, 300, 64, sigma_qk=3.0), 0.125
+    yield "sigma1", make_random(904, 2, 1, 257, 64), 0.125
+    yield "rising", _ramp("rising"), 1.0
+    yield "falling", _ramp("falling"), 1.0
+
+
+LAZY_CASES = list(_cases())
+
+
+@pytest.mark.parametrize("window", [(-1, -1), (-1, 0), (40, 7)], ids=["plain", "causal", "window"])
+@pytest.mark.parametrize("BN,group", [(64, 32), (64, 1), (16, 32), (77, 16)])
+@pytest.mark.parametrize("name,qkv,scale", LAZY_CASES, ids=[c[0] for c in LAZY_CASES])
+def test_lazy_reference_is_exact_algebra(name, qkv, scale, BN, group, window):
+    """Without fp16 rounding of p, keeping the reference lazily reaches the
+    plain definition to rounding (the common reference of o and l cancels):
+    the algebra the kernel's rule relies on, for several tile widths and row
+    groupings."""
+    q, k, v = qkv
+    O, L = oracle.attention_ex(q, k, v, scale, window=window)
+    Om, Lm, _ = lazy_reference_attention(q, k, v, False, scale, BN, group, p_fp16=False, window=window)
+    assert np.max(np.abs(Om - O)) <= 1e-12
+    assert np.max(np.abs(Lm - L) / np.maximum(1.0, np.abs(L))) <= 1e-12
+
+
+@pytest.mark.parametrize("window", [(-1, -1), (-1, 0), (40, 7)], ids=["plain", "causal", "window"])
+@pytest.mark.parametrize("name,qkv,scale", LAZY_CASES, ids=[c[0] for c in LAZY_CASES])
+def test_lazy_reference_with_fp16_p_meets_the_tolerances(name, qkv, scale, window):
+    """With p rounded to fp16 (the operand of the PV product, and what l sums),
+    the kernel's rule at its tiling (64-key tiles, 32-row waves) stays within
+    the parity tolerances of the GPU tests: max |dO| <= 4e-3,
+    mean |dO| <= 5e-4, max |dLSE| <= 1e-3."""
+    q, k, v = qkv
+    O, L = oracle.attention_ex(q, k, v, scale, window=window)
+    Om, Lm, _ = lazy_reference_attention(q, k, v, False, scale, 64, 32, p_fp16=True, window=window)
+    dO = np.abs(Om - O)
+    assert np.all(np.isfinite(Om)) and np.all(np.isfinite(Lm))
+    assert dO.max() <= 4e-3 and dO.mean() <= 5e-4
+    assert np.max(np.abs(Lm - L)) <= 1e-3
+
+
+def test_lazy_reference_moves_only_when_needed():
+    """Falling keys: only the first tile of each row group rebases. Rising
+    keys: every tile does (each raises the maximum by about 180 base-2 units,
+    far past 2^15). iid N(0,1) inputs at scale 1/8: almost never after the
+    first tile."""
+    S = 576
+    tiles = S // 64
+    _, _, reb = lazy_reference_attention(*_ramp("falling", S=S), False, 1.0, 64, 32)
+    assert np.all(reb == 1)
+    _, _, reb = lazy_reference_attention(*_ramp("rising", S=S), False, 1.0, 64, 32)
+    assert np.all(reb == tiles)
+    # a ragged last tile of 3 keys raises the maximum by only 3 keys' worth
+    # (about 8.7 base-2 units), which fp16 holds: it is accepted without a rebase
+    _, _, reb = lazy_reference_attention(*_ramp("rising", S=515), False, 1.0, 64, 32)
+    assert np.all(reb == 8)
+    q, k, v = make_random(905, 1, 2, 1024, 64)
+    _, _, reb = lazy_reference_attention(q, k, v, False, 0.125, 64, 32)
+    assert reb.mean() < 1.5
+
+
+def test_lazy_reference_check_is_what_keeps_p_finite():
+    """Accepting every tile after the first (no row-sum check) lets p overflow
+    fp16 on rising keys, and the output is no longer finite: the check is
+    load-bearing. With the check the same inputs match the definition."""
+    q, k, v = _ramp("rising")
+    Om, _, _ = lazy_reference_attention(q, k, v, False, 1.0, 64, 32, check=False)
+    assert not np.all(np.isfinite(Om))
+    O, _ = oracle.attention(q, k, v, False, 1.0)
+    Om, _, _ = lazy_reference_attention(q, k, v, False, 1.0, 64, 32, check=True)
+    assert np.max(np.abs(Om - O)) <= 4e-3
+
+
+def test_lazy_reference_check_catches_an_infinite_p():
+    """A p that overflows fp16 becomes +inf and so does its row sum, which
+    fails the check whatever the limit: 2^15 (the kernel's, which also keeps
+    every accepted p below 2^15) and even an infinite limit give results
+    within the tolerances on rising keys; only dropping the check fails."""
+    q, k, v = _ramp("rising")
+    O, L = oracle.attention(q, k, v, False, 1.0)
+    for limit in (2.0 ** 15, float("inf")):
+        Om, Lm, _ = lazy_reference_attention(q, k, v, False, 1.0, 64, 32, limit=limit)
+        assert np.max(np.abs(Om - O)) <= 4e-3
+        assert np.max(np.abs(Lm - L)) <= 1e-3

@@ -261,30 +261,36 @@ def test_dropout_zero_is_plain():
     assert np.array_equal(O1.view(np.uint16), O2.view(np.uint16))
 
 
-# ---- the feature workloads at full size (sampled rows) ----
+# ---- the feature workloads at full size (every element) ----
 
 @pytest.mark.parametrize("key", sorted(FEATURES))
-def test_feature_workload_sampled(key):
+def test_feature_workload_whole_tensor(key):
     f = FEATURES[key]
     log(f"case feature workload {key}: {f.name}")
-    g = np.random.Generator(np.random.PCG64(82_000))
+    scale = float(np.float32(f.scale))
     if f.packed:
         q, k, v, cu = make_feature_inputs(key)
         O, L = gpu_varlen(q, k, v, cu, False, f.window, f.dropout_p, f.seed, 0, f.scale)
-        # the oracle on three whole sequences: the shortest, the longest and one more
-        lens = np.diff(cu)
-        for s in sorted({int(np.argmin(lens)), int(np.argmax(lens)), 5}):
-            a, e = int(cu[s]), int(cu[s + 1])
-            sub_cu = np.array([0, e - a], dtype=np.int32)
-            Oref, Lref = oracle.attention_varlen(q[a:e], k[a:e], v[a:e], sub_cu, float(np.float32(f.scale)),
-                                                 window=f.window)
-            check(O[a:e], L[:, a:e], Oref, Lref, f"{key} sequence {s} (rows {a}..{e - 1})")
-        return
-    q, k, v = make_feature_inputs(key)
-    O, L = gpu_ex(q, k, v, False, f.window, f.dropout_p, f.seed, 0, f.scale)
-    rows = np.unique(np.concatenate([g.integers(0, f.B * f.H * f.S, size=96),
-                                     [0, f.S - 1, f.B * f.H * f.S - 1]]))
-    Oref, Lref = oracle.attention_ex(q, k, v, float(np.float32(f.scale)), window=f.window, dropout_p=f.dropout_p,
-                                     seed=f.seed, offset=0, rows=rows)
-    check(O.reshape(-1, f.D)[rows], L.reshape(-1)[rows], Oref, Lref, f"{key} sampled rows")
-    assert np.all(np.isfinite(O)) and np.all(np.isfinite(L))
+        Oref, Lref = oracle.attention_varlen(q, k, v, cu, scale, window=f.window, dropout_p=f.dropout_p,
+                                             seed=f.seed, offset=0)
+    else:
+        q, k, v = make_feature_inputs(key)
+        O, L = gpu_ex(q, k, v, False, f.window, f.dropout_p, f.seed, 0, f.scale)
+        Oref, Lref = oracle.attention_ex(q, k, v, scale, window=f.window, dropout_p=f.dropout_p, seed=f.seed,
+                                         offset=0)
+    check(O, L, Oref, Lref, f"{key} whole tensor")
+
+
+def test_packed_causal_full_height():
+    """Packed causal batch whose sequences average more than 4095 rows: it
+    takes the full-height workgroups (shorter averages take half height), with
+    ragged sequence ends; plain and with dropout, every element."""
+    lens = [4100, 5001, 4500]
+    assert sum(lens) / len(lens) > 4095
+    q, k, v, cu = make_packed(83_000, lens, 8, 2, 64)
+    scale = 0.125
+    for p in (0.0, float(np.float32(0.2))):
+        log(f"case packed causal full height lens={lens} p={p}")
+        O, L = gpu_varlen(q, k, v, cu, True, None, dropout_p=p, seed=21, offset=4, scale=scale)
+        Oref, Lref = oracle.attention_varlen(q, k, v, cu, scale, window=(-1, 0), dropout_p=p, seed=21, offset=4)
+        check(O, L, Oref, Lref, f"packed causal full height p={p}")
