@@ -150,6 +150,13 @@ __device__ __forceinline__ float sum_xor32(float x) {
 // it and knows its value wherever else M0 may be needed.
 //   dma_16B_s: address = 64-bit wave-uniform base (SGPRs) + 32-bit lane offset.
 //   dma_16B_v: full 64-bit per-lane address.
+// Hazards the compiler cannot see through the asm, so the asm pays them itself:
+//   * a VALU write of an SGPR (the v_readfirstlane that moves the base into
+//     SGPRs) followed by a vector-memory instruction that reads that SGPR
+//     needs 5 wait states: s_nop 4 before the SGPR-based load, whatever the
+//     compiler scheduled just before the asm;
+//   * a write of M0 followed by an LDS-DMA load needs 1 wait state: covered by
+//     the same s_nop 4, and by s_nop 0 in the VGPR-addressed form.
 __device__ __forceinline__ void dma_16B_s(const void* sbase_in, uint32_t voff, uint32_t lds_base) {
     // The base is wave-uniform; say so, so it is kept in SGPRs as the
     // instruction requires.
@@ -159,9 +166,8 @@ __device__ __forceinline__ void dma_16B_s(const void* sbase_in, uint32_t voff, u
     const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
     const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
     const void* sbase = reinterpret_cast<const void*>((hi << 32) | lo);
-    // s_nop: one wait state between the write of M0 and the load that reads it
     asm volatile(
-        "s_nop 0\n\t"
+        "s_nop 4\n\t"
         "global_load_lds_dwordx4 %0, %1"
         :
         : "v"(voff), "s"(sbase), "{m0}"(lds_base)
