@@ -65,6 +65,7 @@ typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half4 __attribute__((ext_vector_type(4)));
 typedef _Float16 half2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) void lds_void;
@@ -80,9 +81,10 @@ constexpr float kMaxInit = -1.0e30f;
 // 65504).
 constexpr float kSpeculateLimit = 32768.0f;
 
-template <int D_, int QB_, int NW_, int BN_, int SUB_>
+template <int D_, int QB_, int NW_, int BN_, int SUB_, int MF_ = 16>
 struct Shape {
     static constexpr int D = D_;
+    static constexpr int MF = MF_;            // MFMA shape: 16 (16x16x32) or 32 (32x32x16)
     static constexpr int QB = QB_;            // 16-query blocks per wave
     static constexpr int NW = NW_;            // waves per workgroup
     static constexpr int BN = BN_;            // keys per compute tile
@@ -105,6 +107,7 @@ struct Shape {
     static_assert(BN % 32 == 0 && D % 32 == 0, "tile shape");
     static_assert((LTILE / 8) % (64 * NW) == 0, "loads must divide evenly among lanes");
     static_assert(BN % 16 == 0, "swizzles repeat every 16 rows, so sub-tiles share them");
+    static_assert(MF == 16 || (MF == 32 && D == 64 && QB == 2), "the 32x32x16 path tiles 32 query rows at D = 64");
 };
 
 // XOR swizzles of the 16-byte chunk index within a row, chosen so that the 16
@@ -119,6 +122,11 @@ template <int D>
 __device__ __forceinline__ int swz_v(int row) {
     return D == 64 ? (((row >> 1) & 3) << 1) : ((row & 7) << 1);
 }
+// V swizzle of the 32x32x16 path (D = 64): one transposing-read half-wave
+// reads 4 consecutive rows x 4 consecutive chunks (64 bytes of each row); rows
+// of equal parity share a 256-byte bank window, so rows 2 and 3 of each group
+// of 4 take the other half of the row: chunk index xor 4.
+__device__ __forceinline__ int swz_v32(int row) { return ((row >> 1) & 1) << 2; }
 
 // max / sum over lanes {l, l^16} and {l, l^32}. Both swap results hold the two
 // partners in the same order on every lane, so all four lanes of a query get
@@ -393,6 +401,9 @@ void fa2_fwd_kernel(KernelArgs a) {
     constexpr int NKB = SH::NKB, NKC = SH::NKC, DK = SH::DK, DB = SH::DB, CPR = SH::CPR;
     constexpr int TILE = SH::TILE, LTILE = SH::LTILE, LOADS = SH::LOADS, SUB = SH::SUB, KB = SH::KB;
     constexpr bool ROWSUM_MFMA = FA2_MFMA_ROWSUM == 1 || (FA2_MFMA_ROWSUM == 2 && (D == 128 || MASK == kNoMask));
+    // 32x32x16 MFMAs (D = 64; the dropout instances keep the 16x16x32 path,
+    // whose lane pairs share the generator's draws)
+    constexpr bool MF32 = SH::MF == 32 && !DROP;
 
     // LDS ring: [stage][K | V][LTILE] halves; a stage holds SUB compute tiles.
     extern __shared__ __attribute__((aligned(16))) _Float16 smem[];
@@ -451,7 +462,7 @@ void fa2_fwd_kernel(KernelArgs a) {
     const int row0 = (wave * 64 + lane) / CPR;
     const int pc0 = lane % CPR;
     const uint32_t offK = 2u * (row0 * kv_sr + 8 * (pc0 ^ swz_k<D>(row0)));
-    const uint32_t offV = 2u * (row0 * kv_sr + 8 * (pc0 ^ swz_v<D>(row0)));
+    const uint32_t offV = 2u * (row0 * kv_sr + 8 * (pc0 ^ (MF32 ? swz_v32(row0) : swz_v<D>(row0))));
 
     // Issue the direct-to-LDS loads of K/V stage t (keys t*KB ..) into ring stage
     // ST. Rows past the end of the sequence (only in the last stage) are clamped
@@ -492,6 +503,223 @@ void fa2_fwd_kernel(KernelArgs a) {
     };
 
     issue_tile(t_begin, Int<0>{});
+
+    if constexpr (MF32) {
+    // ---- the 32x32x16 path (D = 64 without dropout) ----
+    // Lane layouts of v_mfma_f32_32x32x16_f16 (32x16 A, 16x32 B, 32x32 C):
+    //   A[i][k] -> lane i + 32*(k/8), element k%8
+    //   B[k][j] -> lane j + 32*(k/8), element k%8
+    //   C[i][j] -> lane j + 32*((i/4)%2), element i%4 + 4*(i/8)
+    // With S^T = K Q^T a lane holds one query (lane%32) and, of each 32-key
+    // block, keys 8t + 4h + e (h = lane/32) in element 4t + e: 32 scores per
+    // lane per 64-key tile, two lanes (l, l^32) per query. For the PV product
+    // over 16-key step w of a block, elements 8w .. 8w+7 of a lane are keys
+    // {16w + 4h + 0..3, 16w + 8 + 4h + 0..3}; taken in that order as the 8
+    // k-values of the lane they are the B operand P^T directly, and the V^T A
+    // operand uses the same key order (two transposing reads of 4 rows). Each
+    // MFMA does twice the work of a 16x16x32 one for the same issue cost, which
+    // the softmax's VALU work competes with.
+    constexpr int DS = D / 16;     // k-steps of one 32x32x16 score block
+    constexpr int NB32 = BN / 32;  // 32-key blocks per compute tile
+    constexpr int DB32 = D / 32;   // 32-row blocks of O^T
+    const int l32 = lane & 31, hh = lane >> 5;
+
+    half8 qreg[DS];
+    {
+        const int row = min(qw0 + l32, len - 1);
+#pragma unroll
+        for (int st = 0; st < DS; ++st)
+            qreg[st] = *reinterpret_cast<const half8*>(Qh + (long long)row * q_sr + 16 * st + 8 * hh);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // Q only (see the 16x16x32 path)
+
+    f32x16 oacc[DB32];
+#pragma unroll
+    for (int db = 0; db < DB32; ++db) oacc[db] = f32x16{};
+    float mc_run = kMaxInit, l_run = 0.f;
+    // Row sums on the matrix unit: a 16x16x32 MFMA whose B operand is one P^T
+    // fragment of this layout. Its B[k][j] sits in lane j + 16*(k/8), so k-group
+    // G = k/8 holds query j + 16*(G%2) (of half G/2). An A operand of ones where
+    // (k/8)%2 == i%2 and zeros elsewhere makes output row i the sum over query
+    // j + 16*(i%2); in the 16x16 C layout lane L finds its own query's sum in
+    // element (L/16)%2. A[i][k] sits in lane i + 16*(k/8): each lane holds 8
+    // equal values, ones where (L/16)%2 == L%2.
+    half8 kSumSel;
+    {
+        const uint32_t v = (((lane >> 4) ^ lane) & 1) ? 0u : 0x3c003c00u;
+        typedef uint32_t u32x4w __attribute__((ext_vector_type(4)));
+        kSumSel = __builtin_bit_cast(half8, u32x4w{v, v, v, v});
+    }
+    bool fresh = true;
+
+    // Tile-independent LDS read offsets (bytes). K: row l32 of a block, logical
+    // chunk 2*step + h; the step only flips bits the row term leaves clear:
+    // offset(step) = rdK ^ (step << 5). V: source lane (column half G, index i)
+    // of a transposing read points at row 4h + i/4 (+8 for the second read) and
+    // columns 16G + 4(i%4) .. +3; the column block db flips chunk bit 2:
+    // offset(db) = rdV ^ (db << 6).
+    const uint32_t rdK = 2u * (l32 * D) + 16u * (hh ^ swz_k<D>(l32));
+    const uint32_t rdV = [&] {
+        const int i = lane & 15, G = (lane >> 4) & 1;
+        const int r = 4 * hh + (i >> 2);
+        return 2u * (r * D) + 16u * ((2 * G + ((i & 3) >> 1)) ^ swz_v32(r)) + 8u * (i & 1);
+    }();
+
+    auto compute_tile32 = [&](const int k0, const char* const ldsK, const char* const ldsV)
+                              __attribute__((always_inline)) {
+        uint32_t rk = rdK, rv = rdV;
+        asm volatile("" : "+v"(rk), "+v"(rv));
+
+        // ---- S^T = K Q^T ----
+        if (FA2_SETPRIO) __builtin_amdgcn_s_setprio(FA2_PRIO_QK);
+        f32x16 sacc[NB32];
+#pragma unroll
+        for (int st = 0; st < DS; ++st)
+#pragma unroll
+            for (int kb = 0; kb < NB32; ++kb) {
+                const half8 ka = *reinterpret_cast<const half8*>(ldsK + (rk ^ (st << 5)) + kb * 32 * D * 2);
+                sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka, qreg[st], st == 0 ? f32x16{} : sacc[kb],
+                                                                  0, 0, 0);
+            }
+        if (FA2_SETPRIO) __builtin_amdgcn_s_setprio(FA2_PRIO_SM);
+
+        // ---- masks ----
+        bool need_mask = k0 + BN > len;
+        if (MASK == kCausal) need_mask |= k0 + BN - 1 > qw0;
+        if (MASK == kWindow) need_mask |= (k0 < qw0 + QW - 1 - a.wl) || (k0 + BN - 1 > qw0 + a.wr);
+        if (need_mask) {
+            const int qrow = qw0 + l32;
+#pragma unroll
+            for (int kb = 0; kb < NB32; ++kb)
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int key = k0 + 32 * kb + 8 * t + 4 * hh + e;
+                        bool out = key >= len;
+                        if (MASK == kCausal) out |= key > qrow;
+                        if (MASK == kWindow) out |= (key < qrow - a.wl) || (key > qrow + a.wr);
+                        if (out) sacc[kb][4 * t + e] = -INFINITY;
+                    }
+        }
+
+        // ---- online softmax, the same lazy reference as the 16x16x32 path ----
+        half8 pb[NB32][2];
+        float rs;
+        auto exponentiate = [&]() __attribute__((always_inline)) {
+            const float mc = mc_run;
+#pragma unroll
+            for (int kb = 0; kb < NB32; ++kb)
+#pragma unroll
+                for (int w = 0; w < 2; ++w) {
+                    half2 h[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][8 * w + 2 * e], a.c, -mc));
+                        const float p1 =
+                            __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][8 * w + 2 * e + 1], a.c, -mc));
+                        h[e] = half2{(_Float16)p0, (_Float16)p1};
+                    }
+                    pb[kb][w] = half8{h[0][0], h[0][1], h[1][0], h[1][1], h[2][0], h[2][1], h[3][0], h[3][1]};
+                }
+            f32x4 ls = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kb = 0; kb < NB32; ++kb)
+#pragma unroll
+                for (int w = 0; w < 2; ++w) ls = __builtin_amdgcn_mfma_f32_16x16x32_f16(kSumSel, pb[kb][w], ls, 0, 0, 0);
+            rs = (lane & 16) ? ls[1] : ls[0];
+        };
+        bool move_ref = fresh;
+        if (!move_ref) {
+            exponentiate();
+            // An overflowed p makes its query's sum inf and, through the zero
+            // weights of the selecting operand (0 * inf), the other query's sum
+            // NaN. Compared as unsigned integers (the sums are never negative)
+            // both are above the bound, a test that does not depend on NaN
+            // semantics.
+            move_ref = __builtin_amdgcn_ballot_w64(__float_as_uint(rs) >= __float_as_uint(kSpeculateLimit)) != 0;
+        }
+        if (move_ref) {
+            float m0 = fmaxf(sacc[0][0], sacc[0][1]);
+            float m1 = fmaxf(sacc[0][2], sacc[0][3]);
+#pragma unroll
+            for (int kb = 0; kb < NB32; ++kb)
+#pragma unroll
+                for (int e = (kb == 0 ? 4 : 0); e < 16; e += 2) {
+                    m0 = fmaxf(m0, sacc[kb][e]);
+                    m1 = fmaxf(m1, sacc[kb][e + 1]);
+                }
+            const float m_new = fmaxf(mc_run, max_xor32(fmaxf(m0, m1)) * a.c);
+            const float alpha = __builtin_amdgcn_exp2f(mc_run - m_new);
+            mc_run = m_new;
+            l_run *= alpha;
+#pragma unroll
+            for (int db = 0; db < DB32; ++db) oacc[db] *= alpha;
+            exponentiate();
+        }
+        fresh = false;
+        l_run += rs;
+
+        // ---- O^T += V^T P^T ----
+        if (FA2_SETPRIO) __builtin_amdgcn_s_setprio(FA2_PRIO_PV);
+#pragma unroll
+        for (int kb = 0; kb < NB32; ++kb)
+#pragma unroll
+            for (int w = 0; w < 2; ++w)
+#pragma unroll
+                for (int db = 0; db < DB32; ++db) {
+                    const char* p0 = ldsV + (rv ^ (db << 6)) + (32 * kb + 16 * w) * D * 2;
+                    const s16x4 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p0);
+                    const s16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0 + 8 * D * 2));
+                    const half4 h0 = __builtin_bit_cast(half4, t0);
+                    const half4 h1 = __builtin_bit_cast(half4, t1);
+                    const half8 va = half8{h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
+                    oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, pb[kb][w], oacc[db], 0, 0, 0);
+                }
+        if (FA2_SETPRIO) __builtin_amdgcn_s_setprio(0);
+    };
+
+    auto tile_step32 = [&](int t, auto st_c) {
+        constexpr int ST = decltype(st_c)::value;
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (t + 1 < t_end) issue_tile(t + 1, Int<1 - ST>{});
+#pragma unroll
+        for (int j = 0; j < SUB; ++j) {
+            const int k0 = t * KB + j * BN;
+            if (k0 >= kend) break;
+            if (MASK == kCausal && k0 > qw0 + QW - 1) break;
+            if (MASK == kWindow) {
+                if (k0 > qw0 + QW - 1 + a.wr) break;
+                if (k0 + BN - 1 < qw0 - a.wl) continue;
+            }
+            compute_tile32(k0, reinterpret_cast<const char*>(smem) + 2 * ((ST * 2 + 0) * LTILE + j * TILE),
+                           reinterpret_cast<const char*>(smem) + 2 * ((ST * 2 + 1) * LTILE + j * TILE));
+        }
+    };
+    for (int t = t_begin; t < t_end; t += 2) {
+        tile_step32(t, Int<0>{});
+        if (t + 1 < t_end) tile_step32(t + 1, Int<1>{});
+    }
+
+    // ---- epilogue: O = o / l in fp16, LSE = scale*m + ln(l) ----
+    _Float16* __restrict__ Oh = a.o + b * a.q_sb + h * a.q_sh + (long long)start * q_sr;
+    float* __restrict__ Lh = a.lse + b * a.l_sb + h * a.l_sh + start;
+    const float inv = 1.0f / l_run;
+    const int row = qw0 + l32;
+    if (row < len) {
+#pragma unroll
+        for (int db = 0; db < DB32; ++db)
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const f32x16 ov = oacc[db];
+                const half4 hv = half4{(_Float16)(ov[4 * t] * inv), (_Float16)(ov[4 * t + 1] * inv),
+                                       (_Float16)(ov[4 * t + 2] * inv), (_Float16)(ov[4 * t + 3] * inv)};
+                *reinterpret_cast<half4*>(Oh + (long long)row * q_sr + 32 * db + 8 * t + 4 * hh) = hv;
+            }
+        if (hh == 0) Lh[row] = (mc_run + log2f(l_run)) * kLn2;
+    }
+    } else {  // ---- the 16x16x32 path ----
 
     // Q^T as the B operand of the score MFMA, kept in registers for the whole scan.
     // Rows past the end are clamped (their results are never stored).
@@ -880,6 +1108,7 @@ void fa2_fwd_kernel(KernelArgs a) {
             if (g == 0) Lh[row] = (mc_run[qb] + log2f(lt)) * kLn2;
         }
     }
+    }  // the 16x16x32 path
 }
 
 // Tile shapes per head dimension: <D, 16-query blocks per wave, waves, keys per
@@ -906,10 +1135,14 @@ void fa2_fwd_kernel(KernelArgs a) {
 #ifndef FA2_D64_SUB
 #define FA2_D64_SUB 2
 #endif
+// MFMA shape of the D = 64 instances without dropout: 16 (16x16x32) or 32 (32x32x16)
+#ifndef FA2_D64_MF
+#define FA2_D64_MF 16
+#endif
 #ifndef FA2_D128_SUB
 #define FA2_D128_SUB 2
 #endif
-using Shape64 = Shape<64, FA2_D64_QB, FA2_D64_NW, FA2_D64_BN, FA2_D64_SUB>;
+using Shape64 = Shape<64, FA2_D64_QB, FA2_D64_NW, FA2_D64_BN, FA2_D64_SUB, FA2_D64_MF>;
 using Shape128 = Shape<128, FA2_D128_QB, FA2_D128_NW, FA2_D128_BN, FA2_D128_SUB>;
 // Half-height workgroups (4 waves, 128 query rows, one compute tile per ring
 // stage) for causal launches whose full-height grid fits in one round of
@@ -918,7 +1151,7 @@ using Shape128 = Shape<128, FA2_D128_QB, FA2_D128_NW, FA2_D128_BN, FA2_D128_SUB>
 // workgroup height halves. Larger causal grids are balanced by the
 // heaviest-first order; they keep the full-height tiles unless the sequences
 // are short (causal_half_height).
-using Shape64c = Shape<64, FA2_D64_QB, 4, FA2_D64_BN, 1>;
+using Shape64c = Shape<64, FA2_D64_QB, 4, FA2_D64_BN, 1, FA2_D64_MF>;
 using Shape128c = Shape<128, FA2_D128_QB, 4, FA2_D128_BN, 1>;
 
 constexpr int kCUs = 256;                 // MI355X compute units
