@@ -66,5 +66,14 @@ def build_all(verbose: bool = False) -> list:
 
 
 if __name__ == "__main__":
-    for path in build_all(verbose=True):
-        print(path)
+    import argparse
+    ap = argparse.ArgumentParser(description="Build libfa2.so (and its poisoned-LDS debug variant) for gfx950.")
+    ap.add_argument("--out", help="build only the main library, to this path (a variant build for comparisons)")
+    ap.add_argument("--define", action="append", default=[], metavar="NAME=VALUE",
+                    help="preprocessor definition for a variant build, e.g. FA2_D64_MF=32 (with --out)")
+    args = ap.parse_args()
+    if args.out:
+        print(build(args.out, [f"-D{d}" for d in args.define], verbose=True))
+    else:
+        for path in build_all(verbose=True):
+            print(path)

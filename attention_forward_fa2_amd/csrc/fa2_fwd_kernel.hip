@@ -588,18 +588,24 @@ void fa2_fwd_kernel(KernelArgs a) {
         if (MASK == kCausal) need_mask |= k0 + BN - 1 > qw0;
         if (MASK == kWindow) need_mask |= (k0 < qw0 + QW - 1 - a.wl) || (k0 + BN - 1 > qw0 + a.wr);
         if (need_mask) {
+            // admissible keys [lo, hi) per row, as in the 16x16x32 path
             const int qrow = qw0 + l32;
+            const int base = k0 + 4 * hh;
+            int hi = len;
+            if (MASK == kCausal) hi = min(hi, qrow + 1);
+            if (MASK == kWindow) hi = min(hi, qrow + a.wr + 1);
+            hi -= base;
+            const int lo = MASK == kWindow ? max(0, qrow - a.wl) - base : 0;
+            const uint32_t width = (uint32_t)max(hi - lo, 0);
 #pragma unroll
             for (int kb = 0; kb < NB32; ++kb)
 #pragma unroll
                 for (int t = 0; t < 4; ++t)
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        const int key = k0 + 32 * kb + 8 * t + 4 * hh + e;
-                        bool out = key >= len;
-                        if (MASK == kCausal) out |= key > qrow;
-                        if (MASK == kWindow) out |= (key < qrow - a.wl) || (key > qrow + a.wr);
-                        if (out) sacc[kb][4 * t + e] = -INFINITY;
+                        const int off = 32 * kb + 8 * t + e;
+                        const bool keep = MASK == kWindow ? (uint32_t)(off - lo) < width : off < hi;
+                        if (!keep) sacc[kb][4 * t + e] = -INFINITY;
                     }
         }
 
@@ -817,18 +823,30 @@ void fa2_fwd_kernel(KernelArgs a) {
         if (MASK == kCausal) need_mask |= k0 + BN - 1 > qw0;
         if (MASK == kWindow) need_mask |= (k0 < qw0 + QW - 1 - a.wl) || (k0 + BN - 1 > qw0 + a.wr);
         if (need_mask) {
+            // The admissible keys of a row are one range, [lo, hi): hi =
+            // min(len, i+1) causal, min(len, i+wr+1) windowed, len otherwise;
+            // lo = max(0, i-wl) windowed, else 0. Element (kb, e) of a lane is
+            // key k0 + 4g + (16kb + e), so per lane the range shifts by
+            // k0 + 4g once and each element compares its constant offset:
+            // one compare (two for a window, as one unsigned range test) and
+            // one select per score.
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb) {
                 const int qrow = qw0 + 16 * qb + l16;
+                const int base = k0 + 4 * g;
+                int hi = len;
+                if (MASK == kCausal) hi = min(hi, qrow + 1);
+                if (MASK == kWindow) hi = min(hi, qrow + a.wr + 1);
+                hi -= base;
+                const int lo = MASK == kWindow ? max(0, qrow - a.wl) - base : 0;
+                const uint32_t width = (uint32_t)max(hi - lo, 0);
 #pragma unroll
                 for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        const int key = k0 + 16 * kb + 4 * g + e;
-                        bool out = key >= len;
-                        if (MASK == kCausal) out |= key > qrow;
-                        if (MASK == kWindow) out |= (key < qrow - a.wl) || (key > qrow + a.wr);
-                        if (out) sacc[qb][kb][e] = -INFINITY;
+                        const int off = 16 * kb + e;
+                        const bool keep = MASK == kWindow ? (uint32_t)(off - lo) < width : off < hi;
+                        if (!keep) sacc[qb][kb][e] = -INFINITY;
                     }
             }
         }
@@ -913,9 +931,15 @@ void fa2_fwd_kernel(KernelArgs a) {
         // round's 64-bit product for every chunk position of a stage live
         // across the scan (16 VGPRs), which spills.
         asm volatile("" : "+v"(group));
+        // The lane's row within its 16-row block, recomputed here from the
+        // lane mask count rather than kept live across the scan: held in a
+        // register it is spilled, and its reload's wait for vector memory
+        // also waits for the next stage's K/V loads.
+        uint32_t lane_now;
+        asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane_now));
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
-            const uint32_t qrow = (uint32_t)(qw0 + 16 * qb + l16);
+            const uint32_t qrow = (uint32_t)(qw0 + 16 * qb) + (lane_now & 15u);
             const U32x4 r = philox4x32_10(group, qrow, (uint32_t)bh, a.offset, a.seed_lo, a.seed_hi);
             // after the swaps: x = this lane's two words for the first
             // block, y = for the second

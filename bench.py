@@ -20,6 +20,7 @@ Prints one JSON line:
     python bench.py [--gpus 1] [--steps 200] [--warmup 200] [--settle-ms 500] [--workload 2] [--causal]
                     [--graph 100]
     python bench.py --feature {gqa,mqa,window,varlen,dropout} [--causal]
+    python bench.py --compare LIB1,LIB2 [--workload N] [--causal] [--steps K] [--block 20]
 
 --feature times one of the production-feature workloads (GQA/MQA, local
 window, packed variable-length sequences, dropout) through fa2_fwd_ex /
@@ -180,37 +181,55 @@ def feature_setup(key: str, causal: bool, dev):
     return f, step, 4.0 * f.D * pairs, cfg, cpu
 
 
-def gemm_calibration(reps: int) -> None:
-    """Median rate of plain fp16/bf16 matrix products through torch (hipBLASLt), one
-    JSON line each: what a vendor GEMM sustains on this GPU, the practical
-    MFMA ceiling beside the 2516.6 TFLOP/s dense fp16 peak. The last two are the
-    attention-shaped products of the unfused path (S = Q K^T, then P V) at
-    B*H = 32, S = 4096, D = 64."""
+def compare_builds(args) -> None:
+    """Launches of one plain workload interleaved over several builds of
+    libfa2, in blocks: one JSON line per build with its median per-launch time
+    (HIP events around each block). The dispatch order is deterministic: after
+    the settling launches (build 0, a multiple of the block), build i runs
+    blocks i, i+n, i+2n, ... of every round."""
     import torch
+    import attention_forward_fa2_amd as fa2
+    from fa2_inputs import WORKLOADS, make_inputs
+    paths = [os.path.abspath(p) for p in args.compare.split(",")]
+    libs = [fa2.load_library(p) for p in paths]
+    w = WORKLOADS[args.workload]
+    causal = bool(args.causal) or w.causal_modes == (True,)
     dev = torch.device("cuda:0")
-    cases = [(dt, (m, n, k), 1) for dt in (torch.float16, torch.bfloat16)
-             for (m, n, k) in ((4096, 4096, 4096), (8192, 8192, 8192), (16384, 16384, 8192))]
-    cases += [(torch.float16, (4096, 4096, 64), 32), (torch.float16, (4096, 64, 4096), 32)]
-    for dt, (m, n, k), batch in cases:
-        g = torch.Generator(device=dev).manual_seed(7)
-        a = torch.randn(batch, m, k, device=dev, dtype=dt, generator=g)
-        b = torch.randn(batch, k, n, device=dev, dtype=dt, generator=g)
-        fn = (lambda: torch.matmul(a[0], b[0])) if batch == 1 else (lambda: torch.bmm(a, b))
-        for _ in range(50):  # lets the clock settle, as for the attention kernel
-            fn()
+    q, k, v = (torch.from_numpy(x).to(dev) for x in make_inputs(args.workload))
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.S), dtype=torch.float32, device=dev)
+    sp = torch.cuda.current_stream(dev).cuda_stream
+
+    def launch(lib):
+        st = lib.fa2_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), w.B, w.H, w.S,
+                         w.D, int(causal), w.scale, sp)
+        if st != 0:
+            raise fa2.FA2Error(st)
+    settle = 0
+    s0 = time.perf_counter()
+    while (time.perf_counter() - s0) * 1e3 < args.settle_ms:
+        for _ in range(args.block):
+            launch(libs[0])
         torch.cuda.synchronize()
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-        for e0, e1 in ev:
-            e0.record()
-            fn()
-            e1.record()
-        torch.cuda.synchronize()
-        ms = sorted(e0.elapsed_time(e1) for e0, e1 in ev)[reps // 2]
-        tf = 2.0 * batch * m * n * k / (ms * 1e-3) / 1e12
-        print(json.dumps({"gemm": f"{batch}x{m}x{n}x{k}", "dtype": str(dt).replace("torch.", ""),
-                          "median_us": round(ms * 1e3, 1), "tflops": round(tf, 1),
-                          "frac_of_2516.6": round(tf / 2516.6, 3)}), flush=True)
-        del a, b
+        settle += args.block
+    times = [[] for _ in libs]
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    rounds = max(1, args.steps // args.block)
+    for _ in range(rounds):
+        for i, lib in enumerate(libs):
+            ev[0].record()
+            for _ in range(args.block):
+                launch(lib)
+            ev[1].record()
+            ev[1].synchronize()
+            times[i].append(ev[0].elapsed_time(ev[1]) * 1e3 / args.block)
+    flops = w.flops(causal)
+    for i, p in enumerate(paths):
+        med = sorted(times[i])[len(times[i]) // 2]
+        print(json.dumps({"compare": p, "workload": f"{w.name} {'causal' if causal else 'non-causal'}",
+                          "settle_launches": settle, "block": args.block, "rounds": rounds, "build_index": i,
+                          "median_us_per_launch": round(med, 2), "tflops": round(flops / (med * 1e-6) / 1e12, 1)}),
+              flush=True)
 
 
 def main():
@@ -239,14 +258,16 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the benchmark, run 10 plain device-to-device copies of MIB MiB "
                          "(the reference kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
-    ap.add_argument("--gemm-calibration", action="store_true",
-                    help="instead of the benchmark, time plain fp16/bf16 matrix products through torch "
-                         "(hipBLASLt): the MFMA rate a vendor GEMM sustains on this GPU")
+    ap.add_argument("--library", metavar="PATH",
+                    help="run this build of libfa2 instead of the in-tree one (a variant made with "
+                         "`python -m attention_forward_fa2_amd.build --out PATH --define NAME=VALUE`)")
+    ap.add_argument("--compare", metavar="PATH1,PATH2,...",
+                    help="instead of the benchmark, interleave the workload's launches over several builds of "
+                         "libfa2 in blocks of --block launches (build i runs blocks i, i+n, i+2n, ... after "
+                         "--settle-ms of clock settling), and print each build's median per-launch time; under "
+                         "rocprofv3 --pmc GRBM_GUI_ACTIVE this gives each build's cycles and clock per launch")
+    ap.add_argument("--block", type=int, default=20, help="launches per block of --compare")
     args = ap.parse_args()
-
-    if args.gemm_calibration:
-        gemm_calibration(max(args.steps, 5))
-        return
 
     if args.copy_calibration:
         import torch
@@ -269,6 +290,13 @@ def main():
     import torch
     import attention_forward_fa2_amd as fa2
     from fa2_inputs import WORKLOADS, make_inputs
+
+    if args.compare:
+        compare_builds(args)
+        return
+    if args.library:
+        fa2._lib = fa2.load_library(os.path.abspath(args.library))
+        log(f"bench: library {args.library}")
 
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream(dev)

@@ -525,3 +525,44 @@ def test_dropout_counter_names_the_register_key():
                     t = key % 8
                     assert grp == key // 8, (k0, kc, l, x)
                     assert (word, half) == (t // 2, t % 2), (k0, kc, l, x)
+
+
+@pytest.mark.parametrize("mode", ["none", "causal", "window"])
+def test_mask_range_form_equals_the_per_key_rule(mode):
+    """The kernel masks a tile's scores with one range test per element: per
+    lane the admissible keys of row i are [lo, hi) (hi = min(len, i+1) causal,
+    min(len, i+wr+1) windowed, len otherwise; lo = max(0, i-wl) windowed, else
+    0), shifted by the lane's first key k0 + 4g; element offset o is kept when
+    o < hi (unsigned o - lo < max(hi - lo, 0) windowed). That must equal the
+    rule key < len and key <= i (causal) or i-wl <= key <= i+wr (window) for
+    every key, including rows whose band misses the tile, ragged tails and the
+    32x32x16 layout's offsets (32kb + 8t + e from k0 + 4h)."""
+    g = np.random.Generator(np.random.PCG64(77 + len(mode)))
+    offs16 = np.array([16 * kb + e for kb in range(4) for e in range(4)])
+    offs32 = np.array([32 * kb + 8 * t + e for kb in range(2) for t in range(4) for e in range(4)])
+    for _ in range(4000):
+        ln = int(g.integers(1, 400))
+        k0 = int(g.integers(0, (ln + 63) // 64)) * 64
+        qrow = int(g.integers(0, ln + 40))
+        wl, wr = int(g.integers(0, 300)), int(g.integers(0, 300))
+        for lanebase, offs in ((4 * int(g.integers(0, 4)), offs16), (4 * int(g.integers(0, 2)), offs32)):
+            base = k0 + lanebase
+            hi = ln
+            if mode == "causal":
+                hi = min(hi, qrow + 1)
+            if mode == "window":
+                hi = min(hi, qrow + wr + 1)
+            hi -= base
+            lo = max(0, qrow - wl) - base if mode == "window" else 0
+            width = max(hi - lo, 0)
+            if mode == "window":
+                keep = ((offs - lo) & 0xFFFFFFFF) < width
+            else:
+                keep = offs < hi
+            key = base + offs
+            rule = key < ln
+            if mode == "causal":
+                rule &= key <= qrow
+            if mode == "window":
+                rule &= (key >= qrow - wl) & (key <= qrow + wr)
+            assert np.array_equal(keep, rule), (mode, ln, k0, qrow, wl, wr, lanebase)
