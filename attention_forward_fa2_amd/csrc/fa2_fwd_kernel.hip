@@ -931,15 +931,9 @@ void fa2_fwd_kernel(KernelArgs a) {
         // round's 64-bit product for every chunk position of a stage live
         // across the scan (16 VGPRs), which spills.
         asm volatile("" : "+v"(group));
-        // The lane's row within its 16-row block, recomputed here from the
-        // lane mask count rather than kept live across the scan: held in a
-        // register it is spilled, and its reload's wait for vector memory
-        // also waits for the next stage's K/V loads.
-        uint32_t lane_now;
-        asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane_now));
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
-            const uint32_t qrow = (uint32_t)(qw0 + 16 * qb) + (lane_now & 15u);
+            const uint32_t qrow = (uint32_t)(qw0 + 16 * qb + l16);
             const U32x4 r = philox4x32_10(group, qrow, (uint32_t)bh, a.offset, a.seed_lo, a.seed_hi);
             // after the swaps: x = this lane's two words for the first
             // block, y = for the second
