@@ -15,6 +15,10 @@ LIB = os.path.join(PKG, "libfa2.so")
 # Debug build for the race check: every LDS ring stage is filled with NaN
 # before each refill (FA2_POISON_LDS); only the tests load it.
 POISON_LIB = os.path.join(PKG, "libfa2_poison.so")
+# Variant with 32x32x16 MFMAs for the D = 64 instances without dropout
+# (FA2_D64_MF=32): fewer cycles per launch, but measured slower because the
+# GPU holds a lower clock under it; kept for that comparison, parity-tested.
+MF32_LIB = os.path.join(PKG, "libfa2_mf32.so")
 SOURCES = ["fa2_api.hip", "fa2_fwd_kernel.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -58,16 +62,18 @@ def build_poison(out: str = POISON_LIB, verbose: bool = False) -> str:
 
 
 def build_all(verbose: bool = False) -> list:
-    """Both libraries, compiled concurrently."""
+    """The library and its two variants, compiled concurrently."""
     from concurrent.futures import ThreadPoolExecutor
-    with ThreadPoolExecutor(2) as ex:
-        futs = [ex.submit(build, LIB, None, verbose), ex.submit(build_poison, POISON_LIB, verbose)]
+    with ThreadPoolExecutor(3) as ex:
+        futs = [ex.submit(build, LIB, None, verbose), ex.submit(build_poison, POISON_LIB, verbose),
+                ex.submit(build, MF32_LIB, ["-DFA2_D64_MF=32"], verbose)]
         return [f.result() for f in futs]
 
 
 if __name__ == "__main__":
     import argparse
-    ap = argparse.ArgumentParser(description="Build libfa2.so (and its poisoned-LDS debug variant) for gfx950.")
+    ap = argparse.ArgumentParser(description="Build libfa2.so and its two variants (poisoned LDS, 32x32x16 MFMAs) "
+                                             "for gfx950.")
     ap.add_argument("--out", help="build only the main library, to this path (a variant build for comparisons)")
     ap.add_argument("--define", action="append", default=[], metavar="NAME=VALUE",
                     help="preprocessor definition for a variant build, e.g. FA2_D64_MF=32 (with --out)")

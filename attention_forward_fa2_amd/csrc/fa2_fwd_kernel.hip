@@ -80,6 +80,17 @@ constexpr float kMaxInit = -1.0e30f;
 // sum) below this bound means none of them overflowed fp16 (largest finite
 // 65504).
 constexpr float kSpeculateLimit = 32768.0f;
+// A rebase sets the reference this far (base-2 units) above the tile's row
+// maximum: the tile's probabilities are then at most 2^-8, which keeps every
+// key within 6 units of the maximum in the normal fp16 range, and later tiles
+// may rise 15 + 8 units above that maximum before a p could overflow, which
+// halves the rebases of peaked rows (scores with a standard deviation of 13
+// base-2 units: 4.4 -> 2.0 per 32-row wave over 1000 keys in the fp64 model
+// of this rule, with the same error).
+#ifndef FA2_REF_HEADROOM
+#define FA2_REF_HEADROOM 8.0f
+#endif
+constexpr float kRefHeadroom = FA2_REF_HEADROOM;
 
 template <int D_, int QB_, int NW_, int BN_, int SUB_, int MF_ = 16>
 struct Shape {
@@ -655,7 +666,7 @@ void fa2_fwd_kernel(KernelArgs a) {
                     m0 = fmaxf(m0, sacc[kb][e]);
                     m1 = fmaxf(m1, sacc[kb][e + 1]);
                 }
-            const float m_new = fmaxf(mc_run, max_xor32(fmaxf(m0, m1)) * a.c);
+            const float m_new = fmaxf(mc_run, __builtin_fmaf(max_xor32(fmaxf(m0, m1)), a.c, kRefHeadroom));
             const float alpha = __builtin_amdgcn_exp2f(mc_run - m_new);
             mc_run = m_new;
             l_run *= alpha;
@@ -863,7 +874,7 @@ void fa2_fwd_kernel(KernelArgs a) {
     // sums the tile's full row sums) stay below 2^15, so no p overflowed.
     // A wave's first tile, or a tile that fails the check for any of its
     // rows, takes the row max (combined over the 4 lanes of a query),
-    // moves the reference to max(m, max), rescales o and l by
+    // moves the reference to max(m, max + kRefHeadroom), rescales o and l by
     // alpha = 2^((m_old - m_new)*c) and exponentiates again: the update
     // of the online softmax.
 
@@ -900,11 +911,10 @@ void fa2_fwd_kernel(KernelArgs a) {
         }
         return max_xor32(max_xor16(fmaxf(a0, a1)));
     };
-    // Move the reference of query block qb up to the raw score mx (if
-    // higher), rescaling o and l. Rounding is monotonic, so max(m*c, mx*c)
-    // is the scaled maximum exactly.
+    // Move the reference of query block qb up to kRefHeadroom above the raw
+    // score mx (if higher), rescaling o and l.
     auto move_reference = [&](int qb, float mx) __attribute__((always_inline)) {
-        const float m_new = fmaxf(mc_run[qb], mx * a.c);
+        const float m_new = fmaxf(mc_run[qb], __builtin_fmaf(mx, a.c, kRefHeadroom));
         const float alpha = __builtin_amdgcn_exp2f(mc_run[qb] - m_new);
         mc_run[qb] = m_new;
         l_run[qb] *= alpha;

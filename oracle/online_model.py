@@ -69,7 +69,7 @@ def online_attention(q, k, v, causal: bool, scale: float, BN: int):
 
 def lazy_reference_attention(q, k, v, causal: bool, scale: float, BN: int, rows_per_group: int = 32,
                              p_fp16: bool = True, check: bool = True, limit: float = 2.0 ** 15,
-                             window=(-1, -1)):
+                             window=(-1, -1), headroom: float = 0.0):
     """The recurrence above with the reference kept lazily, as the GPU kernel
     runs it. Returns O [B,H,S,D], LSE [B,H,S] (float64) and the number of
     rebases per (b, h, row group).
@@ -95,7 +95,10 @@ def lazy_reference_attention(q, k, v, causal: bool, scale: float, BN: int, rows_
     whose keys are all masked so far has alpha = 1 and p = 0. With
     ``check=False`` step 2 accepts every tile (used to show that the check is
     what keeps p finite). ``window`` is (left, right) with -1 unbounded;
-    ``causal`` is the same as (-1, 0)."""
+    ``causal`` is the same as (-1, 0). ``headroom`` (base-2 units, >= 0) sets
+    the reference that far above the tile maximum at each rebase, so that
+    later tiles may rise 15 + headroom units before p overflows; the
+    probabilities are then at most 2^-headroom."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
@@ -144,7 +147,7 @@ def lazy_reference_attention(q, k, v, causal: bool, scale: float, BN: int, rows_
                         rs = p.sum(axis=1)
                         accept = (not check) or bool(np.all(rs < limit))
                     if not accept:
-                        m_new = np.maximum(mc, s.max(axis=1) * c)
+                        m_new = np.maximum(mc, s.max(axis=1) * c + headroom)
                         alpha = np.exp2(mc - m_new)
                         o *= alpha[:, None]
                         l *= alpha

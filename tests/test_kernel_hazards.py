@@ -27,11 +27,11 @@ def _flags():
     return [f for f in b.FLAGS if f not in ("-shared", "-fPIC")]
 
 
-@pytest.fixture(scope="module", params=["normal", "poison"])
+@pytest.fixture(scope="module", params=["normal", "poison", "mf32"])
 def kernel_asm(request, tmp_path_factory):
     from attention_forward_fa2_amd import build as b
     out = tmp_path_factory.mktemp("asm") / "k.s"
-    extra = ["-DFA2_POISON_LDS=1"] if request.param == "poison" else []
+    extra = {"normal": [], "poison": ["-DFA2_POISON_LDS=1"], "mf32": ["-DFA2_D64_MF=32"]}[request.param]
     cmd = [b.HIPCC, *_flags(), *extra, "--offload-device-only", "-S", KERNEL, "-o", str(out)]
     subprocess.run(cmd, check=True, capture_output=True, text=True)
     return out.read_text()

@@ -46,6 +46,10 @@ def test_skipping_the_rescale_breaks_it():
 
 from oracle.online_model import lazy_reference_attention  # noqa: E402
 
+# The kernel sets the reference 8 base-2 units above the tile maximum at each
+# rebase (so probabilities are at most 2^-8 right after it).
+KERNEL_HEADROOM = 8.0
+
 
 def _ramp(direction, S=515, D=64, H=2, seed=902):
     """Scores that rise (or fall) by about 180 base-2 units per 64 keys at
@@ -70,17 +74,19 @@ def _cases():
 LAZY_CASES = list(_cases())
 
 
+@pytest.mark.parametrize("headroom", [0.0, KERNEL_HEADROOM])
 @pytest.mark.parametrize("window", [(-1, -1), (-1, 0), (40, 7)], ids=["plain", "causal", "window"])
 @pytest.mark.parametrize("BN,group", [(64, 32), (64, 1), (16, 32), (77, 16)])
 @pytest.mark.parametrize("name,qkv,scale", LAZY_CASES, ids=[c[0] for c in LAZY_CASES])
-def test_lazy_reference_is_exact_algebra(name, qkv, scale, BN, group, window):
+def test_lazy_reference_is_exact_algebra(name, qkv, scale, BN, group, window, headroom):
     """Without fp16 rounding of p, keeping the reference lazily reaches the
     plain definition to rounding (the common reference of o and l cancels):
     the algebra the kernel's rule relies on, for several tile widths and row
     groupings."""
     q, k, v = qkv
     O, L = oracle.attention_ex(q, k, v, scale, window=window)
-    Om, Lm, _ = lazy_reference_attention(q, k, v, False, scale, BN, group, p_fp16=False, window=window)
+    Om, Lm, _ = lazy_reference_attention(q, k, v, False, scale, BN, group, p_fp16=False, window=window,
+                                         headroom=headroom)
     assert np.max(np.abs(Om - O)) <= 1e-12
     assert np.max(np.abs(Lm - L) / np.maximum(1.0, np.abs(L))) <= 1e-12
 
@@ -94,7 +100,8 @@ def test_lazy_reference_with_fp16_p_meets_the_tolerances(name, qkv, scale, windo
     mean |dO| <= 5e-4, max |dLSE| <= 1e-3."""
     q, k, v = qkv
     O, L = oracle.attention_ex(q, k, v, scale, window=window)
-    Om, Lm, _ = lazy_reference_attention(q, k, v, False, scale, 64, 32, p_fp16=True, window=window)
+    Om, Lm, _ = lazy_reference_attention(q, k, v, False, scale, 64, 32, p_fp16=True, window=window,
+                                         headroom=KERNEL_HEADROOM)
     dO = np.abs(Om - O)
     assert np.all(np.isfinite(Om)) and np.all(np.isfinite(Lm))
     assert dO.max() <= 4e-3 and dO.mean() <= 5e-4
@@ -144,3 +151,21 @@ def test_lazy_reference_check_catches_an_infinite_p():
         Om, Lm, _ = lazy_reference_attention(q, k, v, False, 1.0, 64, 32, limit=limit)
         assert np.max(np.abs(Om - O)) <= 4e-3
         assert np.max(np.abs(Lm - L)) <= 1e-3
+
+
+def test_reference_headroom_halves_rebases_of_peaked_rows():
+    """Scores with a standard deviation of about 13 base-2 units (Q, K ~ N(0, 3^2),
+    D = 64, scale 1/8) keep raising the row maximum over 1000 keys: with the
+    reference at the tile maximum each 32-row group rebases about 4.4 times,
+    with it 8 units above about 2.0 times, and the result stays within the
+    parity tolerances; with 12 or more units the fp16 subnormal range starts
+    to cost accuracy, which is why the kernel stops at 8."""
+    q, k, v = make_random(906, 1, 4, 1000, 64, sigma_qk=3.0)
+    O, L = oracle.attention(q, k, v, False, 0.125)
+    res = {}
+    for hr in (0.0, KERNEL_HEADROOM, 14.0):
+        Om, Lm, reb = lazy_reference_attention(q, k, v, False, 0.125, 64, 32, headroom=hr)
+        res[hr] = (reb.mean(), np.abs(Om - O).max(), np.abs(Lm - L).max())
+    assert res[KERNEL_HEADROOM][0] < 0.6 * res[0.0][0]
+    assert res[KERNEL_HEADROOM][1] <= 4e-3 and res[KERNEL_HEADROOM][2] <= 1e-3
+    assert res[14.0][1] > 2 * res[KERNEL_HEADROOM][1]
