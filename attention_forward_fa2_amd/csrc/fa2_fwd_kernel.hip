@@ -502,13 +502,18 @@ void fa2_fwd_kernel(KernelArgs a) {
                 dma_16B_s(Vh + rows * kv_sr, offV, dst + 2u * (ST * 2 + 1) * LTILE);
             }
         } else {
+            // (opaque copies of the lane offsets: otherwise the compiler keeps
+            // the per-lane 64-bit addresses Kh + offK, Vh + offV live across
+            // the whole scan for this one stage)
+            uint32_t oK = offK, oV = offV;
+            asm volatile("" : "+v"(oK), "+v"(oV));
 #pragma unroll
             for (int i = 0; i < LOADS; ++i) {
                 const int r = row0 + i * ROWS_PER_LOAD;
                 const long long shift = (long long)(min(k0 + r, len - 1) - row0) * kv_sr;
                 const uint32_t dst = lds_base + 2u * (i * NW + wave) * 512;
-                dma_16B_v((const char*)(Kh + shift) + offK, dst + 2u * (ST * 2 + 0) * LTILE);
-                dma_16B_v((const char*)(Vh + shift) + offV, dst + 2u * (ST * 2 + 1) * LTILE);
+                dma_16B_v((const char*)(Kh + shift) + oK, dst + 2u * (ST * 2 + 0) * LTILE);
+                dma_16B_v((const char*)(Vh + shift) + oV, dst + 2u * (ST * 2 + 1) * LTILE);
             }
         }
     };
@@ -1117,6 +1122,12 @@ void fa2_fwd_kernel(KernelArgs a) {
     // ---- epilogue: O = o / l in fp16, LSE = scale*m + ln(l) ----
     _Float16* __restrict__ Oh = a.o + b * a.q_sb + h * a.q_sh + (long long)start * q_sr;
     float* __restrict__ Lh = a.lse + b * a.l_sb + h * a.l_sh + start;
+    // The lane's row and column terms, derived again here from an opaque copy
+    // of the lane index: otherwise the compiler keeps them live across the
+    // scan and, at the 128-register budget, spills one to scratch.
+    int lane_e = lane;
+    asm volatile("" : "+v"(lane_e));
+    const int l16e = lane_e & 15, ge = lane_e >> 4;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
         // l_run holds per-lane partial sums (4 lanes per query) unless the row
@@ -1124,16 +1135,16 @@ void fa2_fwd_kernel(KernelArgs a) {
         float lt = l_run[qb];
         if (!ROWSUM_MFMA) lt = sum_xor32(sum_xor16(lt));
         const float inv = (DROP ? a.out_scale : 1.0f) / lt;
-        const int row = qw0 + 16 * qb + l16;
+        const int row = qw0 + 16 * qb + l16e;
         if (row < len) {
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
                 const f32x4 ov = oacc[db][qb];
                 const half4 hv = half4{(_Float16)(ov[0] * inv), (_Float16)(ov[1] * inv),
                                        (_Float16)(ov[2] * inv), (_Float16)(ov[3] * inv)};
-                *reinterpret_cast<half4*>(Oh + (long long)row * q_sr + 16 * db + 4 * g) = hv;
+                *reinterpret_cast<half4*>(Oh + (long long)row * q_sr + 16 * db + 4 * ge) = hv;
             }
-            if (g == 0) Lh[row] = (mc_run[qb] + log2f(lt)) * kLn2;
+            if (ge == 0) Lh[row] = (mc_run[qb] + log2f(lt)) * kLn2;
         }
     }
     }  // the 16x16x32 path
