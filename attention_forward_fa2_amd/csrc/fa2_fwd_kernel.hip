@@ -507,10 +507,16 @@ void fa2_fwd_kernel(KernelArgs a) {
             // the whole scan for this one stage)
             uint32_t oK = offK, oV = offV;
             asm volatile("" : "+v"(oK), "+v"(oV));
+            // The lane's load row again, from a lane index the compiler cannot
+            // hoist: otherwise it keeps row0 live across the scan for this one
+            // stage and spills it.
+            int ln;
+            asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
+            const int r0 = (wave * 64 + ln) / CPR;
 #pragma unroll
             for (int i = 0; i < LOADS; ++i) {
-                const int r = row0 + i * ROWS_PER_LOAD;
-                const long long shift = (long long)(min(k0 + r, len - 1) - row0) * kv_sr;
+                const int r = r0 + i * ROWS_PER_LOAD;
+                const long long shift = (long long)(min(k0 + r, len - 1) - r0) * kv_sr;
                 const uint32_t dst = lds_base + 2u * (i * NW + wave) * 512;
                 dma_16B_v((const char*)(Kh + shift) + oK, dst + 2u * (ST * 2 + 0) * LTILE);
                 dma_16B_v((const char*)(Vh + shift) + oV, dst + 2u * (ST * 2 + 1) * LTILE);
@@ -940,7 +946,13 @@ void fa2_fwd_kernel(KernelArgs a) {
     // words it needs. Kept probabilities are scaled by 1/(1-p) in the
     // epilogue.
     auto drop_chunk = [&](const int k0, PBT& pb, int kc) __attribute__((always_inline)) {
-        uint32_t group = (uint32_t)((k0 + 32 * kc) >> 3) + 2u * (uint32_t)(g & 1) + (uint32_t)(g >> 1);
+        // The lane's part of the counter, through an opaque copy: otherwise
+        // the compiler keeps one sum per chunk position live across the scan
+        // and spills them (not needed in the half-height causal instance,
+        // which stays within its registers and runs 1 % faster without it).
+        uint32_t gl = 2u * (uint32_t)(g & 1) + (uint32_t)(g >> 1);
+        if (!(NW == 4 && MASK == kCausal)) asm volatile("" : "+v"(gl));
+        uint32_t group = (uint32_t)((k0 + 32 * kc) >> 3) + gl;
         // Opaque to the optimiser: the counter grows linearly with the
         // tile, and loop strength reduction otherwise keeps the first
         // round's 64-bit product for every chunk position of a stage live

@@ -232,6 +232,65 @@ def compare_builds(args) -> None:
               flush=True)
 
 
+def scan_heads(args) -> None:
+    """One plain workload's B, S, D and input distribution at several head
+    counts, launches interleaved in blocks (as in compare_builds): one JSON
+    line per head count with the workgroup count of its launch and the median
+    per-launch time. Shows how the grid's size, in rounds of resident
+    workgroups, sets the kernel rate."""
+    import torch
+    import attention_forward_fa2_amd as fa2
+    from fa2_inputs import WORKLOADS, make_random
+    w = WORKLOADS[args.workload]
+    causal = bool(args.causal) or w.causal_modes == (True,)
+    heads = [int(x) for x in args.scan_heads.split(",")]
+    dev = torch.device("cuda:0")
+    sp = torch.cuda.current_stream(dev).cuda_stream
+    runs = []
+    for i, H in enumerate(heads):
+        q, k, v = (torch.from_numpy(x).to(dev)
+                   for x in make_random(7000 + 10 * i, w.B, H, w.S, w.D, w.sigma_qk, w.sigma_v))
+        o = torch.empty_like(q)
+        lse = torch.empty((w.B, H, w.S), dtype=torch.float32, device=dev)
+        runs.append((H, q, k, v, o, lse))
+
+    def launch(r):
+        H, q, k, v, o, lse = r
+        st = fa2.fa2_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), w.B, H, w.S, w.D,
+                         int(causal), w.scale, sp)
+        if st != 0:
+            raise fa2.FA2Error(st)
+    s0 = time.perf_counter()
+    settle = 0
+    while (time.perf_counter() - s0) * 1e3 < args.settle_ms:
+        for r in runs:
+            for _ in range(args.block):
+                launch(r)
+        torch.cuda.synchronize()
+        settle += args.block * len(runs)
+    times = [[] for _ in runs]
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    for _ in range(max(1, args.steps // args.block)):
+        for i, r in enumerate(runs):
+            ev[0].record()
+            for _ in range(args.block):
+                launch(r)
+            ev[1].record()
+            ev[1].synchronize()
+            times[i].append(ev[0].elapsed_time(ev[1]) * 1e3 / args.block)
+    for i, r in enumerate(runs):
+        H = r[0]
+        med = sorted(times[i])[len(times[i]) // 2]
+        cfg = fa2.fa2_kernel_config(w.B, H, w.S, w.D, int(causal))
+        flops = 4.0 * w.B * H * w.S * w.S * w.D / (2 if causal else 1)
+        print(json.dumps({"scan_heads": H, "workload": f"B{w.B} H{H} S{w.S} D{w.D} "
+                          f"{'causal' if causal else 'non-causal'}", "settle_launches": settle,
+                          "block": args.block, "workgroups": cfg["blocks"],
+                          "rows_per_workgroup": cfg["rows_per_block"],
+                          "median_us_per_launch": round(med, 2), "tflops": round(flops / (med * 1e-6) / 1e12, 1)}),
+              flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -266,7 +325,10 @@ def main():
                          "libfa2 in blocks of --block launches (build i runs blocks i, i+n, i+2n, ... after "
                          "--settle-ms of clock settling), and print each build's median per-launch time; under "
                          "rocprofv3 --pmc GRBM_GUI_ACTIVE this gives each build's cycles and clock per launch")
-    ap.add_argument("--block", type=int, default=20, help="launches per block of --compare")
+    ap.add_argument("--block", type=int, default=20, help="launches per block of --compare and --scan-heads")
+    ap.add_argument("--scan-heads", metavar="H1,H2,...",
+                    help="time the workload's B, S, D and input distribution at these head counts instead, "
+                         "launches interleaved in blocks; one JSON line per head count")
     args = ap.parse_args()
 
     if args.copy_calibration:
@@ -297,6 +359,9 @@ def main():
     if args.library:
         fa2._lib = fa2.load_library(os.path.abspath(args.library))
         log(f"bench: library {args.library}")
+    if args.scan_heads:
+        scan_heads(args)
+        return
 
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream(dev)
