@@ -10,7 +10,10 @@ flags and checks, in every kernel instance:
   * every global_load_lds is preceded by at least 1 wait state since the last
     write of M0 (the LDS-DMA base);
   * device code has no scalar-memory stores, scalar atomics or scalar-cache
-    write-backs (s_store*, s_atomic*, s_dcache_wb*).
+    write-backs (s_store*, s_atomic*, s_dcache_wb*);
+  * the library's own build uses no scratch: no spilled VGPRs and a zero
+    private segment in every instance (a spill reload waits on the same
+    vector-memory counter as the K/V prefetch).
 """
 import os
 import re
@@ -106,3 +109,14 @@ def test_no_scalar_cache_writes(kernel_asm):
     bad = [ins for _, body in _instances(kernel_asm) for ins in body
            if re.match(r"s_(store|atomic|dcache_wb|buffer_store|scratch_store)", ins)]
     assert not bad, bad[:5]
+
+
+def test_library_build_uses_no_scratch(kernel_asm, request):
+    if request.node.callspec.params["kernel_asm"] != "normal":
+        pytest.skip("only the library's own build is held to this")
+    names = re.findall(r"\.name:\s+(_Z\S*fa2_fwd_kernel\S*)", kernel_asm)
+    private = re.findall(r"\.private_segment_fixed_size:\s+(\d+)", kernel_asm)
+    spills = re.findall(r"\.vgpr_spill_count:\s+(\d+)", kernel_asm)
+    assert len(names) == len(private) == len(spills) == 24
+    bad = [(n, p, v) for n, p, v in zip(names, private, spills) if int(p) or int(v)]
+    assert not bad, bad
