@@ -281,6 +281,27 @@ def test_feature_workload_whole_tensor(key):
     check(O, L, Oref, Lref, f"{key} whole tensor")
 
 
+@pytest.mark.parametrize("key", ["dropout", "varlen", "window"])
+def test_feature_workload_whole_tensor_causal(key):
+    """The causal side of the feature workloads, as the bench runs them with
+    --causal: the window's right edge at 0 (for an unbounded window, causal)."""
+    f = FEATURES[key]
+    win = (f.window[0], 0)
+    log(f"case feature workload {key} causal: {f.name}, window {win}")
+    scale = float(np.float32(f.scale))
+    if f.packed:
+        q, k, v, cu = make_feature_inputs(key)
+        O, L = gpu_varlen(q, k, v, cu, False, win, f.dropout_p, f.seed, 0, f.scale)
+        Oref, Lref = oracle.attention_varlen(q, k, v, cu, scale, window=win, dropout_p=f.dropout_p,
+                                             seed=f.seed, offset=0)
+    else:
+        q, k, v = make_feature_inputs(key)
+        O, L = gpu_ex(q, k, v, False, win, f.dropout_p, f.seed, 0, f.scale)
+        Oref, Lref = oracle.attention_ex(q, k, v, scale, window=win, dropout_p=f.dropout_p, seed=f.seed,
+                                         offset=0)
+    check(O, L, Oref, Lref, f"{key} causal whole tensor")
+
+
 def test_packed_causal_full_height():
     """Packed causal batch whose sequences average more than 4095 rows: it
     takes the full-height workgroups (shorter averages take half height), with
