@@ -398,8 +398,9 @@ __device__ __forceinline__ U32x4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_
 #define FA2_POISON_LDS 0
 #endif
 
-// Occupancy target of the dropout instances at D=64 (waves per SIMD); the
-// generator's registers do not fit the 4-wave budget without spills.
+// Occupancy target of the dropout instances at D=64 (waves per SIMD). At 4
+// they fit the 128-register budget without spills; 3 (141 registers) was
+// measured 11-12 % slower.
 #ifndef FA2_DROP_WAVES
 #define FA2_DROP_WAVES 4
 #endif
