@@ -20,6 +20,10 @@ POISON_LIB = os.path.join(PKG, "libfa2_poison.so")
 # GPU holds a lower clock under it; kept for that comparison, parity-tested.
 MF32_LIB = os.path.join(PKG, "libfa2_mf32.so")
 SOURCES = ["fa2_api.hip", "fa2_fwd_kernel.hip"]
+# Host-only library over the kernel's index arithmetic (fa2_index.h), for the
+# CPU tests that check their emulation against it.
+INDEX_PROBE_SRC = os.path.join(ROOT, "tests", "index_probe", "fa2_index_probe.hip")
+INDEX_PROBE_LIB = os.path.join(ROOT, "tests", "index_probe", "libfa2_index_probe.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # -packed-fp32-ops: keep hipcc from emitting packed fp32 VALU ops (v_pk_*_f32).
@@ -61,12 +65,27 @@ def build_poison(out: str = POISON_LIB, verbose: bool = False) -> str:
     return build(out, ["-DFA2_POISON_LDS=1"], verbose)
 
 
+def build_index_probe(out: str = INDEX_PROBE_LIB, verbose: bool = False) -> str:
+    """The host-only index probe (no GPU code)."""
+    tmp = out + ".tmp"
+    cmd = [HIPCC, "--offload-arch=gfx950", "-O2", "-std=c++17", "-fPIC", "-shared", "-Wall", "-I", CSRC,
+           INDEX_PROBE_SRC, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{res.stderr}")
+    os.replace(tmp, out)
+    return out
+
+
 def build_all(verbose: bool = False) -> list:
-    """The library and its two variants, compiled concurrently."""
+    """The library, its two variants and the index probe, compiled concurrently."""
     from concurrent.futures import ThreadPoolExecutor
-    with ThreadPoolExecutor(3) as ex:
+    with ThreadPoolExecutor(4) as ex:
         futs = [ex.submit(build, LIB, None, verbose), ex.submit(build_poison, POISON_LIB, verbose),
-                ex.submit(build, MF32_LIB, ["-DFA2_D64_MF=32"], verbose)]
+                ex.submit(build, MF32_LIB, ["-DFA2_D64_MF=32"], verbose),
+                ex.submit(build_index_probe, INDEX_PROBE_LIB, verbose)]
         return [f.result() for f in futs]
 
 

@@ -41,7 +41,7 @@ sys.path.insert(0, ROOT)
 MFMA_F16_PEAK_TFLOPS = 2516.6   # MI355X dense fp16 MFMA, 256 CUs x 2.4 GHz x 4096 FLOP/clk/CU
 HBM_PEAK_GBS = 8000.0
 KERNEL_SOURCES = [os.path.join(ROOT, "attention_forward_fa2_amd", "csrc", f)
-                  for f in ("fa2_fwd_kernel.hip", "fa2_internal.h")]
+                  for f in ("fa2_fwd_kernel.hip", "fa2_index.h", "fa2_internal.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa2_fwd_B4H8S4096D64_noncausal_traffic.json")
 
 

@@ -21,9 +21,19 @@ library uses and checks, for many tensor shapes, that
     256-byte window,
   * the transposing reads deliver V[32kc + 4g + e][16db + lane%16] in element e,
     in the key order of the S^T accumulator (the P handoff).
-If the kernel's formulas change, this file must change with them."""
+The workgroup mapping, the swizzles, the per-lane K/V load offsets and the LDS
+read bases restated here are also compared with the kernel's own code: they
+live in attention_forward_fa2_amd/csrc/fa2_index.h, which a host-only probe
+library (tests/index_probe) compiles for the CPU. The other formulas (the loop
+bounds, masks, stores) are restated only; if they change in the kernel, this
+file must change with them."""
+import ctypes
+import os
+
 import numpy as np
 import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
 def swz_k(D, r):
@@ -32,6 +42,23 @@ def swz_k(D, r):
 
 def swz_v(D, r):
     return (((r >> 1) & 3) << 1) if D == 64 else ((r & 7) << 1)
+
+
+def lane_load_offsets(D, NW, kv_sr, wave, lane):
+    """A lane's first stage row and its K and V source offsets (bytes)."""
+    CPR = D // 8
+    row0, pc0 = (wave * 64 + lane) // CPR, lane % CPR
+    return (row0, 2 * (row0 * kv_sr + 8 * (pc0 ^ swz_k(D, row0))),
+            2 * (row0 * kv_sr + 8 * (pc0 ^ swz_v(D, row0))))
+
+
+def lds_read_bases(D, lane):
+    """The per-lane K and V LDS read bases (bytes) of the 16x16x32 path."""
+    l16, g = lane & 15, lane >> 4
+    rdK0 = 2 * (l16 * D + 8 * (g ^ swz_k(D, l16)))
+    r0v = 4 * g + (l16 >> 2)
+    rdV0 = 2 * (r0v * D + 8 * (((l16 & 3) >> 1) ^ swz_v(D, r0v)) + 4 * (l16 & 1))
+    return rdK0, rdV0
 
 
 # D -> (QB, NW, BN, SUB) of the library's tiles (SUB compute tiles per LDS stage)
@@ -257,16 +284,17 @@ def emulate(B, H, S, D, causal, shape=None, H_kv=None, cu=None, total=None, wind
                     assert off.min() >= 0 and (off + 8).max() <= n_q
                     assert (start + row).min() >= start and (start + row).max() < start + ln
             # K/V direct-to-LDS loads: one lane offset per tensor, scalar steps
-            row0, pc0 = (wave * 64 + lane) // CPR, lane % CPR
+            row0, offK, offV = lane_load_offsets(D, NW, kv_sr, wave, lane)
+            pc0 = lane % CPR
             for i in range(LOADS):
                 c = (i * NW + wave) * 64 + lane
                 r, pc = c // CPR, c % CPR
                 assert np.array_equal(r, row0 + i * RPL) and np.array_equal(pc, pc0)
                 dst = 2 * (i * NW + wave) * 512 + 16 * lane
                 assert dst.min() >= 0 and (dst + 16).max() <= 2 * LTILE
-                for sw in (swz_k, swz_v):
-                    lane_off = row0 * kv_sr + 8 * (pc0 ^ sw(D, row0))
-                    assert (2 * lane_off).max() < 2 ** 32
+                for sw, off in ((swz_k, offK), (swz_v, offV)):
+                    assert off.max() < 2 ** 32
+                    lane_off = off // 2
                     for t in range(t_begin, t_end):
                         k0 = t * KB
                         if k0 + KB <= ln:
@@ -346,9 +374,7 @@ def test_lds_reads_and_bank_groups(D):
     l16, g = lane & 15, lane >> 4
     # the kernel keeps one base per tensor and derives the k-step / column-block
     # offsets by XOR; that must equal the per-row formula
-    rdK0 = 2 * (l16 * D + 8 * (g ^ swz_k(D, l16)))
-    r0v = 4 * g + (l16 >> 2)
-    rdV0 = 2 * (r0v * D + 8 * (((l16 & 3) >> 1) ^ swz_v(D, r0v)) + 4 * (l16 & 1))
+    rdK0, rdV0 = lds_read_bases(D, lane)
     for kk in range(DK):
         hoisted = 2 * (l16 * D + 8 * ((4 * kk + g) ^ swz_k(D, l16)))
         assert np.array_equal(rdK0 ^ (kk << 6), hoisted)
@@ -566,3 +592,120 @@ def test_mask_range_form_equals_the_per_key_rule(mode):
             if mode == "window":
                 rule &= (key >= qrow - wl) & (key <= qrow + wr)
             assert np.array_equal(keep, rule), (mode, ln, k0, qrow, wl, wr, lanebase)
+
+
+# ---- the emulation against the kernel's own index code (fa2_index.h) ----
+
+@pytest.fixture(scope="module")
+def probe():
+    """The host-only probe library over fa2_index.h, rebuilt when older than its sources."""
+    from attention_forward_fa2_amd import build as b
+    srcs = [b.INDEX_PROBE_SRC, os.path.join(b.CSRC, "fa2_index.h")]
+    if not os.path.exists(b.INDEX_PROBE_LIB) or \
+            os.path.getmtime(b.INDEX_PROBE_LIB) < max(os.path.getmtime(x) for x in srcs):
+        b.build_index_probe()
+    lib = ctypes.CDLL(b.INDEX_PROBE_LIB)
+    i, ip, up = ctypes.c_int, ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_uint32)
+    lib.fa2_probe_swizzle.argtypes = [i, i, i]
+    lib.fa2_probe_map_blocks.argtypes = [i] * 9 + [ip, i, i, i, i, ip, ip]
+    lib.fa2_probe_map_blocks.restype = None
+    lib.fa2_probe_lane_load_offsets.argtypes = [i] * 6 + [ip, up, up]
+    lib.fa2_probe_lds_read_bases.argtypes = [i, i, up, up]
+    return lib
+
+
+def kernel_map(lib, mask, nqt, group, BH, serp=0, cu=None, lpt=0, S=0, total=0):
+    """bh, qt per workgroup as the kernel's map_block computes them (-1: no work)."""
+    BHkv = BH // group
+    if cu is None:
+        nb = BH * nqt
+        cu_p, nseq = None, 0
+    else:
+        nb = -(-BHkv // 8) * 8 * nqt * group
+        cu_arr = np.ascontiguousarray(cu, dtype=np.int32)
+        cu_p, nseq = cu_arr.ctypes.data_as(ctypes.POINTER(ctypes.c_int)), len(cu_arr) - 1
+    bh = np.empty(nb, dtype=np.int32)
+    qt = np.empty(nb, dtype=np.int32)
+    H = BH // nseq if cu is not None else BH       # query heads (read by the packed ranking only)
+    lib.fa2_probe_map_blocks(mask, nqt, group, BH, BHkv, H, BH * nqt, serp, lpt, cu_p, nseq, total, S, nb,
+                             bh.ctypes.data_as(ctypes.POINTER(ctypes.c_int)),
+                             qt.ctypes.data_as(ctypes.POINTER(ctypes.c_int)))
+    return bh, qt
+
+
+def test_swizzles_equal_the_kernel(probe):
+    for D in (64, 128):
+        for r in range(512):
+            assert probe.fa2_probe_swizzle(0, D, r) == swz_k(D, r)
+            assert probe.fa2_probe_swizzle(1, D, r) == swz_v(D, r)
+
+
+@pytest.mark.parametrize("BH", list(range(1, 41)) + [96, 192, 256])
+@pytest.mark.parametrize("nqt", [1, 2, 3, 16, 33])
+@pytest.mark.parametrize("mask", [0, 1, 2])
+def test_dense_mapping_equals_the_kernel(probe, BH, nqt, mask):
+    """The emulated mapping is the kernel's, for every workgroup; windows take
+    the non-causal walk."""
+    bh, qt = kernel_map(probe, mask, nqt, 1, BH)
+    ebh, eqt = block_map(BH, nqt, mask == 1)
+    assert np.array_equal(bh, ebh) and np.array_equal(qt, eqt)
+
+
+@pytest.mark.parametrize("BHkv,group", [(8, 1), (16, 1), (8, 4), (24, 2), (12, 2), (1, 32), (32, 1), (4, 4)])
+@pytest.mark.parametrize("nqt", [1, 5, 8, 16, 33, 64])
+@pytest.mark.parametrize("serp", [0, 32])
+def test_gqa_and_serpentine_mapping_equals_the_kernel(probe, BHkv, group, nqt, serp):
+    BH = BHkv * group
+    for mask in (0, 1):
+        bh, qt = kernel_map(probe, mask, nqt, group, BH, serp=serp if mask == 1 else 0)
+        ebh, eqt = block_map(BH, nqt, mask == 1, group, serp=serp if mask == 1 else 0)
+        assert np.array_equal(bh, ebh) and np.array_equal(qt, eqt)
+
+
+@pytest.mark.parametrize("nseq", [1, 2, 7, 24, 64, 70])
+@pytest.mark.parametrize("H_kv,group", [(1, 1), (2, 4), (8, 1)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_packed_mapping_equals_the_kernel(probe, nseq, H_kv, group, causal):
+    """Packed launches, with the longest-first order (up to 64 sequences, lpt)
+    and without it, on tables with ties, empty sequences and a malformed entry
+    (the kernel clamps it)."""
+    g = np.random.Generator(np.random.PCG64(nseq * 7 + H_kv + 100 * causal))
+    lens = [int(x) if g.random() > 0.2 else int(g.choice([0, 5])) for x in g.integers(0, 3000, size=nseq)]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    total, S = int(cu[-1]), max(max(lens), 1)
+    if nseq > 2:
+        cu[2] = cu[1] - 3           # malformed: a start before the previous one
+    BH, nqt = nseq * H_kv * group, 3
+    lpt = int(nseq <= 64)
+    bh, qt = kernel_map(probe, int(causal), nqt, group, BH, cu=cu, lpt=lpt, S=S, total=total)
+    clamped = []
+    for i in range(nseq):
+        s0 = min(max(int(cu[i]), 0), total)
+        clamped.append(min(min(max(int(cu[i + 1]), s0), total) - s0, S))
+    ebh, eqt, ok = block_map_packed(BH, nqt, causal, group, clamped if lpt else None)
+    assert np.array_equal(bh >= 0, ok)
+    assert np.array_equal(bh[ok], ebh[ok]) and np.array_equal(qt[ok], eqt[ok])
+
+
+@pytest.mark.parametrize("D,NW", [(64, 8), (64, 4), (128, 8), (128, 4)])
+@pytest.mark.parametrize("kv_sr_heads", [1, 2, 8, 32])
+def test_lane_load_offsets_equal_the_kernel(probe, D, NW, kv_sr_heads):
+    """Dense (row stride D) and packed (row stride H_kv*D) K/V layouts."""
+    kv_sr = kv_sr_heads * D
+    row0 = ctypes.c_int()
+    offK, offV = ctypes.c_uint32(), ctypes.c_uint32()
+    for wave in range(NW):
+        er, eK, eV = lane_load_offsets(D, NW, kv_sr, wave, np.arange(64))
+        for lane in range(64):
+            assert probe.fa2_probe_lane_load_offsets(D, NW, 0, kv_sr, wave, lane, ctypes.byref(row0),
+                                                     ctypes.byref(offK), ctypes.byref(offV)) == 0
+            assert (row0.value, offK.value, offV.value) == (er[lane], eK[lane], eV[lane])
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_lds_read_bases_equal_the_kernel(probe, D):
+    rk, rv = ctypes.c_uint32(), ctypes.c_uint32()
+    eK, eV = lds_read_bases(D, np.arange(64))
+    for lane in range(64):
+        assert probe.fa2_probe_lds_read_bases(D, lane, ctypes.byref(rk), ctypes.byref(rv)) == 0
+        assert (rk.value, rv.value) == (eK[lane], eV[lane])
