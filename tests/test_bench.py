@@ -1,6 +1,7 @@
 """bench.py's contract: the one-GPU refusal, the traffic record it reports only
 for the kernel source the counters were taken on, the admitted-pair count
-behind the feature FLOPs (CPU), and the JSON line itself (GPU)."""
+behind the feature FLOPs (CPU), the JSON line itself and the lines of the
+build-comparison and head-count modes (GPU)."""
 import json
 import os
 import subprocess
@@ -110,3 +111,30 @@ def test_bench_feature_line():
     assert d["config"]["causal"] is True and d["config"]["sequences"] == 24
     d0 = _run_bench(["--workload", "1", "--steps", "5", "--warmup", "5", "--no-cpu-baseline", "--graph", "0"])
     assert d0["graph_timing"] is None
+
+
+@pytest.mark.gpu
+def test_bench_compare_and_scan_lines():
+    """The two diagnostic modes: one JSON line per build (--compare) and per
+    head count (--scan-heads), each with its median per-launch time."""
+    import attention_forward_fa2_amd as fa2
+    lib = os.path.join(ROOT, "attention_forward_fa2_amd", "libfa2.so")
+    res = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--workload", "4", "--compare",
+                          f"{lib},{lib}", "--steps", "40", "--block", "10", "--settle-ms", "50"],
+                         capture_output=True, text=True, timeout=240, cwd=ROOT)
+    assert res.returncode == 0, res.stderr[-1500:]
+    lines = [json.loads(ln) for ln in res.stdout.splitlines() if ln.strip()]
+    assert [d["build_index"] for d in lines] == [0, 1]
+    for d in lines:
+        assert d["rounds"] == 4 and d["median_us_per_launch"] > 0 and d["tflops"] > 0
+    res = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--workload", "4", "--scan-heads", "4,12",
+                          "--steps", "40", "--block", "10", "--settle-ms", "50"],
+                         capture_output=True, text=True, timeout=240, cwd=ROOT)
+    assert res.returncode == 0, res.stderr[-1500:]
+    lines = [json.loads(ln) for ln in res.stdout.splitlines() if ln.strip()]
+    assert [d["scan_heads"] for d in lines] == [4, 12]
+    for d in lines:
+        assert d["workgroups"] == fa2.fa2_kernel_config(16, d["scan_heads"], 1000, 64, 0)["blocks"]
+        assert d["median_us_per_launch"] > 0
+        flops = 4.0 * 16 * d["scan_heads"] * 1000 * 1000 * 64
+        assert d["tflops"] == pytest.approx(flops / (d["median_us_per_launch"] * 1e-6) / 1e12, rel=2e-3)
