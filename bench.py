@@ -8,9 +8,15 @@ Prints one JSON line:
 
     value      FLOP rate, 4*B*H*S^2*D FLOPs (halved when causal) / average step time
                over K back-to-back steps timed by one pair of HIP events
-    roofline   the kernel against the MI355X dense fp16 MFMA peak (2516.6 TFLOP/s),
-               its duration taken with HIP events around each launch on the
-               launch stream, in a second pass of the same K steps
+    roofline   the kernel against the MI355X dense fp16 MFMA peak (2516.6 TFLOP/s);
+               its duration is the average per launch of the same timed region
+               (back to back on the launch stream, so each launch's time is the
+               kernel plus the short dispatch gap; rocprofv3's kernel trace
+               agrees within about 1 %). With --cold, where a cache-scrubbing
+               fill runs between launches, it is the average of HIP event pairs
+               around each launch, from a second pass of the same K steps
+    launch_timing  both passes: the step time and the per-launch event pairs
+               (which also time each launch's event and dispatch latency)
     cpu_baseline  the fp64 CPU oracle timed on a bounded sample of the same
                workload on this host's cores (a reported baseline, not a target)
     graph_timing  per-launch time of N launches captured in one HIP graph,
@@ -21,6 +27,7 @@ Prints one JSON line:
                     [--graph 100]
     python bench.py --feature {gqa,mqa,window,varlen,dropout} [--causal]
     python bench.py --compare LIB1,LIB2 [--workload N] [--causal] [--steps K] [--block 20]
+    python bench.py --scan-heads H1,H2,... [--workload N] [--causal] [--steps K] [--block 20]
 
 --feature times one of the production-feature workloads (GQA/MQA, local
 window, packed variable-length sequences, dropout) through fa2_fwd_ex /
@@ -412,10 +419,12 @@ def main():
     log(f"bench: clock settling {settle['launches']} launches ({settle['ms']} ms), warmup {args.warmup} done")
 
     # Two timed passes of the same K steps on the launch stream. The first has
-    # only the outer pair of events and gives the step time (value); the second
-    # records an event pair around every launch and gives the kernel duration
-    # (roofline.achieved). Per-launch events are kept out of the first pass
-    # because each one adds a gap of several microseconds between kernels.
+    # only the outer pair of events and gives the step time (value and, warm,
+    # the kernel duration of roofline.achieved: back-to-back launches are the
+    # kernel plus a short dispatch gap). The second records an event pair
+    # around every launch; those pairs also time each launch's event and
+    # dispatch latency (a few microseconds), so they serve only when something
+    # else runs between launches (--cold) and as a reported cross-check.
     scrub = torch.empty(512 << 20, dtype=torch.uint8, device=dev) if args.cold else None
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
@@ -480,8 +489,13 @@ def main():
             f"per launch (min {per[0] * 1e3:.1f}, max {per[-1] * 1e3:.1f})")
         del graph
 
-    achieved = flops / (kern_avg_ms * 1e-3) / 1e12
+    achieved = flops / ((kern_avg_ms if args.cold else ms_per_step) * 1e-3) / 1e12
     value = achieved if args.cold else flops / (ms_per_step * 1e-3) / 1e12
+    launch_timing = {"step_us": round(ms_per_step * 1e3, 2), "event_pair_avg_us": round(kern_avg_ms * 1e3, 2),
+                     "event_pair_min_us": round(kern_ms[0] * 1e3, 2),
+                     "event_pair_median_us": round(kern_ms[len(kern_ms) // 2] * 1e3, 2),
+                     "achieved_from": "event pairs around each launch" if args.cold else
+                     "the step time of back-to-back launches"}
     traffic = None if args.feature else measured_traffic(args.workload, causal)
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_F16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4),
@@ -521,6 +535,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "graph_timing": graph_timing,
+        "launch_timing": launch_timing,
         "clock_settle": {"launches": settle["launches"], "ms": settle["ms"],
                          "note": "untimed launches of the same step before the warmup steps"},
     }

@@ -90,6 +90,13 @@ def test_bench_json_line():
     assert r["bound"] == "mfma" and r["unit"] == "TFLOP/s" and r["peak"] == 2516.6
     assert r["frac"] == pytest.approx(r["achieved"] / r["peak"], abs=1e-4)
     assert 0 < r["frac"] < 1
+    # warm: the kernel duration is the back-to-back step time; the per-launch
+    # event pairs are reported beside it and also time each launch's latency
+    lt = d["launch_timing"]
+    assert r["achieved"] == pytest.approx(d["value"], rel=1e-3)
+    assert lt["step_us"] == pytest.approx(d["ms_per_step"] * 1e3, abs=0.01)
+    assert lt["achieved_from"] == "the step time of back-to-back launches"
+    assert 0 < lt["event_pair_min_us"] <= lt["event_pair_median_us"]
     assert r["traffic"] == bench.measured_traffic(2, False)
     c = d["cpu_baseline"]
     assert c["kind"] == "oracle" and c["unit"] == "TFLOP/s" and c["cores"] >= 1 and c["value"] > 0
