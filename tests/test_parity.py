@@ -41,15 +41,17 @@ def gpu_forward(q, k, v, causal, scale):
     return o.cpu().numpy(), lse.cpu().numpy()
 
 
-def check(O, L, Oref, Lref, what):
+def check(O, L, Oref, Lref, what, dropout_p: float = 0.0):
+    """The three bounds; with dropout the O bounds scale by 1/(1-p), as O does."""
     O64, L64 = O.astype(np.float64), L.astype(np.float64)
     assert np.all(np.isfinite(O64)), f"{what}: non-finite O"
     assert np.all(np.isfinite(L64)), f"{what}: non-finite LSE"
     dO = np.abs(O64 - Oref)
     dL = np.abs(L64 - Lref)
+    amp = 1.0 / (1.0 - dropout_p)
     log(f"  {what}: max|dO|={dO.max():.3e} mean|dO|={dO.mean():.3e} max|dLSE|={dL.max():.3e}")
-    assert dO.max() <= TOL_MAX_O, f"{what}: max|dO| {dO.max():.3e}"
-    assert dO.mean() <= TOL_MEAN_O, f"{what}: mean|dO| {dO.mean():.3e}"
+    assert dO.max() <= TOL_MAX_O * amp, f"{what}: max|dO| {dO.max():.3e}"
+    assert dO.mean() <= TOL_MEAN_O * amp, f"{what}: mean|dO| {dO.mean():.3e}"
     assert dL.max() <= TOL_LSE, f"{what}: max|dLSE| {dL.max():.3e}"
 
 
@@ -241,7 +243,7 @@ def test_full_height_causal_ragged(B, H, S, D, p):
                             seed=0x5EED, offset=11, scale=scale)
     torch.cuda.synchronize()
     Oref, Lref = oracle.attention_ex(q, k, v, scale, window=(-1, 0), dropout_p=p32, seed=0x5EED, offset=11)
-    check(o.cpu().numpy(), lse.cpu().numpy(), Oref, Lref, f"full-height causal S={S} D={D} p={p}")
+    check(o.cpu().numpy(), lse.cpu().numpy(), Oref, Lref, f"full-height causal S={S} D={D} p={p}", p32)
 
 
 @pytest.mark.parametrize("D", [64, 128])

@@ -18,6 +18,16 @@ pytestmark = pytest.mark.gpu
 TOL_MAX_O = 4e-3
 TOL_MEAN_O = 5e-4
 TOL_LSE = 1e-3
+# With dropout every kept value of O is multiplied by 1/(1-p) (O_i = sum_j P_ij z_ij v_j / (1-p)), and
+# so are the absolute rounding errors of O: the O bounds scale by that factor (the LSE, computed before
+# dropout, keeps its bound). At p = 0.5 an fp16 O reaches |O| of 8 and more on peaked rows, where one
+# fp16 step is 2^-7, and the unscaled bound would sit below the output format's own resolution.
+
+
+def o_bounds(dropout_p: float = 0.0):
+    """(max, mean) bounds of |O - O_ref| for a dropout probability."""
+    amp = 1.0 / (1.0 - dropout_p)
+    return TOL_MAX_O * amp, TOL_MEAN_O * amp
 
 
 def log(msg):
@@ -25,15 +35,16 @@ def log(msg):
     sys.stdout.flush()
 
 
-def check(O, L, Oref, Lref, what):
+def check(O, L, Oref, Lref, what, dropout_p: float = 0.0):
     O64, L64 = O.astype(np.float64), L.astype(np.float64)
     assert np.all(np.isfinite(O64)), f"{what}: non-finite O"
     assert np.all(np.isfinite(L64)), f"{what}: non-finite LSE"
     dO = np.abs(O64 - Oref)
     dL = np.abs(L64 - Lref)
+    tol_max, tol_mean = o_bounds(dropout_p)
     log(f"  {what}: max|dO|={dO.max():.3e} mean|dO|={dO.mean():.3e} max|dLSE|={dL.max():.3e}")
-    assert dO.max() <= TOL_MAX_O, f"{what}: max|dO| {dO.max():.3e}"
-    assert dO.mean() <= TOL_MEAN_O, f"{what}: mean|dO| {dO.mean():.3e}"
+    assert dO.max() <= tol_max, f"{what}: max|dO| {dO.max():.3e}"
+    assert dO.mean() <= tol_mean, f"{what}: mean|dO| {dO.mean():.3e}"
     assert dL.max() <= TOL_LSE, f"{what}: max|dLSE| {dL.max():.3e}"
 
 
@@ -74,7 +85,7 @@ def dense_case(q, k, v, causal=False, window=None, dropout_p=0.0, seed=0, offset
     O, L = gpu_ex(q, k, v, causal, window, p32, seed, offset, scale)
     Oref, Lref = oracle.attention_ex(q, k, v, float(np.float32(scale)), window=eff_window(causal, window),
                                      dropout_p=p32, seed=seed, offset=offset)
-    check(O, L, Oref, Lref, what)
+    check(O, L, Oref, Lref, what, p32)
     return O, L
 
 
@@ -240,7 +251,7 @@ def test_dropout_with_window_gqa_and_varlen():
         O, L = gpu_varlen(q, k, v, cu, causal, None, dropout_p=p32, seed=5, offset=9, scale=scale)
         Oref, Lref = oracle.attention_varlen(q, k, v, cu, float(np.float32(scale)),
                                              window=eff_window(causal, None), dropout_p=p32, seed=5, offset=9)
-        check(O, L, Oref, Lref, f"dropout varlen causal={causal}")
+        check(O, L, Oref, Lref, f"dropout varlen causal={causal}", p32)
 
 
 def test_dropout_is_reproducible_and_seeded():
@@ -278,7 +289,7 @@ def test_feature_workload_whole_tensor(key):
         O, L = gpu_ex(q, k, v, False, f.window, f.dropout_p, f.seed, 0, f.scale)
         Oref, Lref = oracle.attention_ex(q, k, v, scale, window=f.window, dropout_p=f.dropout_p, seed=f.seed,
                                          offset=0)
-    check(O, L, Oref, Lref, f"{key} whole tensor")
+    check(O, L, Oref, Lref, f"{key} whole tensor", f.dropout_p)
 
 
 @pytest.mark.parametrize("key", ["dropout", "varlen", "window"])
@@ -299,7 +310,7 @@ def test_feature_workload_whole_tensor_causal(key):
         O, L = gpu_ex(q, k, v, False, win, f.dropout_p, f.seed, 0, f.scale)
         Oref, Lref = oracle.attention_ex(q, k, v, scale, window=win, dropout_p=f.dropout_p, seed=f.seed,
                                          offset=0)
-    check(O, L, Oref, Lref, f"{key} causal whole tensor")
+    check(O, L, Oref, Lref, f"{key} causal whole tensor", f.dropout_p)
 
 
 def test_packed_causal_full_height():
@@ -314,4 +325,4 @@ def test_packed_causal_full_height():
         log(f"case packed causal full height lens={lens} p={p}")
         O, L = gpu_varlen(q, k, v, cu, True, None, dropout_p=p, seed=21, offset=4, scale=scale)
         Oref, Lref = oracle.attention_varlen(q, k, v, cu, scale, window=(-1, 0), dropout_p=p, seed=21, offset=4)
-        check(O, L, Oref, Lref, f"packed causal full height p={p}")
+        check(O, L, Oref, Lref, f"packed causal full height p={p}", p)

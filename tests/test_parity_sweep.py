@@ -17,7 +17,10 @@ from test_parity_features import check, eff_window, gpu_ex, gpu_varlen, log
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 120
+N_CASES = 400
+# Seeds beyond the sweep whose outputs (D = 128, p = 0.48-0.59, |O| up to 8.9) exceed the unscaled
+# O bound and meet the dropout-scaled one: kept to hold that bound to the cases that need it.
+HIGH_DROPOUT = [939, 1589, 1646, 1825, 1893]
 
 
 def sweep_case(i: int) -> dict:
@@ -54,7 +57,10 @@ def case_id(i: int) -> str:
     return f"{i}-D{c['D']}-H{c['H']}kv{c['H_kv']}-{shape}-{mask}-p{c['p']:.2f}".replace(" ", "")
 
 
-@pytest.mark.parametrize("i", range(N_CASES), ids=[case_id(i) for i in range(N_CASES)])
+CASES = list(range(N_CASES)) + HIGH_DROPOUT
+
+
+@pytest.mark.parametrize("i", CASES, ids=[case_id(i) for i in CASES])
 def test_sweep(i):
     c = sweep_case(i)
     log(f"case sweep {case_id(i)} scale={c['scale']} seed={c['seed']} offset={c['offset']}")
@@ -70,4 +76,4 @@ def test_sweep(i):
         O, L = gpu_ex(q, k, v, c["causal"], c["window"], c["p"], c["seed"], c["offset"], c["scale"])
         Oref, Lref = oracle.attention_ex(q, k, v, c["scale"], window=win, dropout_p=c["p"], seed=c["seed"],
                                          offset=c["offset"])
-    check(O, L, Oref, Lref, f"sweep {i}")
+    check(O, L, Oref, Lref, f"sweep {i}", c["p"])
